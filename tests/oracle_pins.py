@@ -1,0 +1,375 @@
+"""Pins for the oracle: checks against what the pages and the mathematics fix.
+
+Each pin takes an ``impl`` namespace holding the functions under test, so the
+same checks run on the real oracle (tests/test_oracle_pins.py) and on copies
+with a planted mistake (tests/test_oracle_mutations.py), which must fail at
+least one pin. Nothing here retypes an oracle formula: the references are
+closed forms, invariants, torch CPU float64 library routines, brute-force
+loops written differently, and the pages' worked numbers.
+"""
+from __future__ import annotations
+
+import cmath
+import json
+import math
+import os
+import types
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import attention as o_attn
+from oracle import epilogue as o_epi
+from oracle import grid as o_grid
+from oracle import modulate as o_mod
+from oracle import rope as o_rope
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def real_impl():
+    return types.SimpleNamespace(
+        num_tokens=o_grid.num_tokens, coords=o_grid.coords, token_of=o_grid.token_of,
+        positions=o_grid.positions, coords_bruteforce=o_grid.coords_bruteforce,
+        layer_norm=o_mod.layer_norm, adaln_modulate=o_mod.adaln_modulate,
+        apply_rope=o_rope.apply_rope,
+        attention=o_attn.attention, attention_bruteforce=o_attn.attention_bruteforce,
+        gated_residual=o_epi.gated_residual, euler_step=o_epi.euler_step,
+        interpolant=o_epi.interpolant, velocity=o_epi.velocity,
+    )
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- grid
+def pin_grid_bruteforce(impl):
+    for (T, H, W) in [(2, 4, 4), (1, 64, 64), (21, 30, 52), (5, 3, 7), (1, 1, 1)]:
+        bf = impl.coords_bruteforce(T, H, W)
+        cf = impl.coords(np.arange(T * H * W), H, W)
+        assert np.array_equal(bf, cf), (T, H, W)
+        assert np.array_equal(impl.token_of(cf, H, W), np.arange(T * H * W))
+
+
+def pin_grid_worked_counts(impl):
+    g = json.load(open(os.path.join(GOLDEN, "worked_counts.json")))
+    vae = g["vae_latent_720p_5s"]
+    lat = [vae["frames"] // vae["factor_t"], vae["height"] // vae["factor_h"],
+           vae["width"] // vae["factor_w"]]
+    assert lat == vae["latent"]
+    assert impl.num_tokens(vae["frames"], vae["height"], vae["width"], vae["factor_t"],
+                           vae["factor_h"], vae["factor_w"]) == 30 * 90 * 160
+    tk = g["tokens_30x90x160_patch2x2"]
+    assert impl.num_tokens(*tk["latent"], *tk["patch"]) == tk["tokens"]
+    assert tk["tokens"] // tk["gpus"] == tk["tokens_per_gpu"]
+    assert tk["heads"] // tk["gpus"] == tk["heads_per_gpu"]
+    px = g["pixel_values_720p_5s"]
+    assert 120 * 3 * 720 * 1280 == px["product"] > px["lower_bound"]
+
+
+def pin_grid_workload_counts(impl):
+    import synth
+    # latent (T, H, W) and patch per workload, from the workload definitions
+    lat = {"c1_tiny_f32": ((2, 8, 8), (1, 2, 2)),
+           "c2_image_4096_bf16": ((1, 128, 128), (1, 2, 2)),
+           "c3_video480p_32760_bf16": ((21, 60, 104), (1, 2, 2)),
+           "c4_video720p_27280_bf16": ((31, 44, 80), (1, 2, 2))}
+    for name, (L, P) in lat.items():
+        w = synth.WORKLOADS[name]
+        assert impl.num_tokens(*L, *P) == w.seqlens[0], name
+    w5 = synth.WORKLOADS["c5_varlen_frames_bf16"]
+    for f, n in zip(w5.frames, w5.seqlens):
+        assert impl.num_tokens(f, 60, 104, 1, 2, 2) == n
+
+
+def pin_grid_varlen_restart(impl):
+    cu = np.array([0, 12, 12 + 20, 12 + 20 + 4])
+    pos = impl.positions(cu, 2, 2)
+    assert np.array_equal(pos[0], [0, 0, 0]) and np.array_equal(pos[12], [0, 0, 0])
+    assert np.array_equal(pos[32], [0, 0, 0])
+    assert np.array_equal(pos[11], [2, 1, 1]) and np.array_equal(pos[31], [4, 1, 1])
+
+
+# ---------------------------------------------------------------- modulate
+def pin_modulate_gamma0(impl):
+    r = _rng(1)
+    x = r.standard_normal((9, 48))
+    g = np.zeros((3, 48))
+    b = r.standard_normal((3, 48))
+    y = impl.adaln_modulate(x, g, b, 3, 1e-6)
+    assert np.array_equal(y, b[np.arange(9) // 3])
+
+
+def pin_modulate_moments(impl):
+    r = _rng(2)
+    x = r.standard_normal((7, 64)) * 0.01 + 3.0  # small variance: eps matters
+    eps = 1e-6
+    y = impl.adaln_modulate(x, np.ones((1, 64)), np.zeros((1, 64)), 7, eps)
+    var_pop = x.var(axis=1)
+    assert np.allclose(y.mean(axis=1), 0.0, atol=1e-12)
+    assert np.allclose(y.var(axis=1), var_pop / (var_pop + eps), rtol=1e-12, atol=0)
+
+
+def pin_modulate_constant_row(impl):
+    x = np.full((4, 32), 0.75)
+    r = _rng(3)
+    g = r.standard_normal((1, 32))
+    b = r.standard_normal((1, 32))
+    y = impl.adaln_modulate(x, g, b, 4, 1e-6)
+    assert np.array_equal(y, np.broadcast_to(b, (4, 32)))
+
+
+def pin_modulate_library(impl):
+    r = _rng(4)
+    x = r.standard_normal((12, 96))
+    g = r.standard_normal((3, 96))
+    b = r.standard_normal((3, 96))
+    y = impl.adaln_modulate(x, g, b, 4, 1e-6)
+    ln = torch.nn.functional.layer_norm(torch.from_numpy(x), (96,), eps=1e-6).numpy()
+    ref = ln * np.repeat(g, 4, axis=0) + np.repeat(b, 4, axis=0)
+    assert np.allclose(y, ref, rtol=0, atol=1e-12)
+
+
+def pin_modulate_bruteforce(impl):
+    r = _rng(5)
+    x = r.standard_normal((3, 10))
+    g = r.standard_normal((3, 10))
+    b = r.standard_normal((3, 10))
+    y = impl.adaln_modulate(x, g, b, 1, 1e-5)
+    for i in range(3):
+        row = [float(v) for v in x[i]]
+        m = math.fsum(row) / len(row)
+        var = math.fsum((v - m) ** 2 for v in row) / len(row)
+        for c in range(10):
+            ref = g[i, c] * (row[c] - m) / math.sqrt(var + 1e-5) + b[i, c]
+            assert abs(y[i, c] - ref) < 1e-12
+
+
+# ---------------------------------------------------------------- rope
+SPLIT = (16, 24, 24)
+
+
+def pin_rope_origin_identity(impl):
+    r = _rng(6)
+    x = r.standard_normal((3, 2, 64))
+    y = impl.apply_rope(x, np.zeros((3, 3)), SPLIT, 10000.0)
+    assert np.array_equal(y, x)
+
+
+def pin_rope_pair_norms(impl):
+    r = _rng(7)
+    x = r.standard_normal((20, 3, 64))
+    pos = r.integers(0, 50, size=(20, 3))
+    y = impl.apply_rope(x, pos, SPLIT, 10000.0)
+    nx = x[..., 0::2] ** 2 + x[..., 1::2] ** 2
+    ny = y[..., 0::2] ** 2 + y[..., 1::2] ** 2
+    assert np.allclose(nx, ny, rtol=1e-12, atol=1e-12)
+
+
+def _rope1d_textbook(vec, pos, d, base):
+    """Text RoPE on one d-wide vector: pair j as a complex number turned by
+    pos / base^(2j/d)."""
+    out = []
+    for j in range(d // 2):
+        zc = complex(vec[2 * j], vec[2 * j + 1]) * cmath.exp(1j * pos / (base ** (2 * j / d)))
+        out += [zc.real, zc.imag]
+    return out
+
+
+def pin_rope_axis_special_cases(impl):
+    r = _rng(8)
+    base = 10000.0
+    offs = (0, SPLIT[0], SPLIT[0] + SPLIT[1])
+    for axis in range(3):
+        for p in (1, 5, 37):
+            pos = np.zeros((1, 3))
+            pos[0, axis] = p
+            x = r.standard_normal((1, 1, 64))
+            y = impl.apply_rope(x, pos, SPLIT, base)
+            lo, hi = offs[axis], offs[axis] + SPLIT[axis]
+            ref = _rope1d_textbook(x[0, 0, lo:hi], p, SPLIT[axis], base)
+            assert np.allclose(y[0, 0, lo:hi], ref, rtol=0, atol=1e-12)
+            rest = np.r_[0:lo, hi:64]
+            assert np.array_equal(y[0, 0, rest], x[0, 0, rest])
+
+
+def pin_rope_relative(impl):
+    r = _rng(9)
+    base = 10000.0
+    q = r.standard_normal((1, 1, 64))
+    k = r.standard_normal((1, 1, 64))
+    for _ in range(5):
+        p = r.integers(0, 30, size=3).astype(float)
+        pp = r.integers(0, 30, size=3).astype(float)
+        sh = r.integers(-10, 40, size=3).astype(float)
+        a = (impl.apply_rope(q, p[None], SPLIT, base) * impl.apply_rope(k, pp[None], SPLIT, base)).sum()
+        b = (impl.apply_rope(q, (p + sh)[None], SPLIT, base) *
+             impl.apply_rope(k, (pp + sh)[None], SPLIT, base)).sum()
+        assert abs(a - b) < 1e-10
+
+
+def pin_rope_composition(impl):
+    r = _rng(10)
+    x = r.standard_normal((4, 2, 64))
+    p1 = r.integers(0, 20, size=(4, 3))
+    p2 = r.integers(0, 20, size=(4, 3))
+    y = impl.apply_rope(impl.apply_rope(x, p1, SPLIT, 500.0), p2, SPLIT, 500.0)
+    z = impl.apply_rope(x, p1 + p2, SPLIT, 500.0)
+    assert np.allclose(y, z, rtol=0, atol=1e-11)
+
+
+# ---------------------------------------------------------------- attention
+def _qkv(seed, n, h=2, d=16, scale=1.0):
+    r = _rng(seed)
+    return [r.standard_normal((n, h, d)) * scale for _ in range(3)]
+
+
+def pin_attn_ones(impl):
+    q, k, _ = _qkv(11, 37)
+    v = np.ones_like(q)
+    o = impl.attention(q, k, v, [0, 37])
+    assert np.allclose(o, 1.0, rtol=0, atol=1e-12)
+
+
+def pin_attn_identical_keys(impl):
+    q, k, v = _qkv(12, 29)
+    k[:] = k[0:1]
+    o = impl.attention(q, k, v, [0, 29])
+    assert np.allclose(o, np.broadcast_to(v.mean(axis=0), o.shape), atol=1e-12)
+
+
+def pin_attn_zero_query(impl):
+    _, k, v = _qkv(13, 23)
+    q = np.zeros_like(k)
+    o = impl.attention(q, k, v, [0, 23])
+    assert np.allclose(o, np.broadcast_to(v.mean(axis=0), o.shape), atol=1e-12)
+
+
+def pin_attn_single_token(impl):
+    q, k, v = _qkv(14, 1)
+    o = impl.attention(q, k, v, [0, 1])
+    assert np.allclose(o, v, atol=1e-14)
+
+
+def pin_attn_dominant_key(impl):
+    q, k, v = _qkv(15, 19)
+    j = 7
+    q[:] = 40.0 * k[j][None] / np.linalg.norm(k[j], axis=-1, keepdims=True)[None]
+    o = impl.attention(q, k, v, [0, 19])
+    # scores for key j exceed the rest by a wide margin -> output is V_j
+    assert np.allclose(o, np.broadcast_to(v[j], o.shape), atol=1e-3)
+
+
+def pin_attn_permutation(impl):
+    q, k, v = _qkv(16, 31)
+    perm = _rng(17).permutation(31)
+    o = impl.attention(q, k, v, [0, 31])
+    o_p = impl.attention(q[perm], k[perm], v[perm], [0, 31])
+    assert np.allclose(o_p, o[perm], atol=1e-12)
+    o_kv = impl.attention(q, k[perm], v[perm], [0, 31])
+    assert np.allclose(o_kv, o, atol=1e-12)
+
+
+def pin_attn_varlen_blocks(impl):
+    q, k, v = _qkv(18, 40)
+    cu = [0, 9, 9 + 17, 40]
+    o = impl.attention(q, k, v, cu)
+    for s in range(3):
+        lo, hi = cu[s], cu[s + 1]
+        oi = impl.attention(q[lo:hi], k[lo:hi], v[lo:hi], [0, hi - lo])
+        assert np.allclose(o[lo:hi], oi, atol=1e-13)
+
+
+def pin_attn_library(impl):
+    q, k, v = _qkv(19, 45, h=3, d=32, scale=1.5)
+    o = impl.attention(q, k, v, [0, 45])
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(1, 0, 2)))  # [h, n, d]
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v)).numpy()
+    assert np.allclose(o, ref.transpose(1, 0, 2), rtol=0, atol=1e-12)
+
+
+def pin_attn_bruteforce(impl):
+    q, k, v = _qkv(20, 11, h=2, d=8)
+    cu = [0, 4, 11]
+    o = impl.attention(q, k, v, cu)
+    ref = np.array(impl.attention_bruteforce(q.tolist(), k.tolist(), v.tolist(), cu))
+    assert np.allclose(o, ref, atol=1e-12)
+
+
+def pin_attn_row_subset(impl):
+    q, k, v = _qkv(21, 50)
+    cu = [0, 20, 50]
+    rows = np.array([0, 3, 19, 20, 33, 49])
+    full = impl.attention(q, k, v, cu)
+    sub = impl.attention(q, k, v, cu, rows=rows)
+    assert np.allclose(sub, full[rows], atol=1e-14)
+
+
+# ---------------------------------------------------------------- epilogue
+def pin_residual_alpha0(impl):
+    r = _rng(22)
+    x = r.standard_normal((6, 32))
+    br = r.standard_normal((6, 2, 16))
+    y = impl.gated_residual(x, br, np.zeros((2, 32)), 3)
+    assert np.array_equal(y, x)
+
+
+def pin_residual_bruteforce(impl):
+    r = _rng(23)
+    x = r.standard_normal((4, 6))
+    br = r.standard_normal((4, 2, 3))
+    a = r.standard_normal((2, 6))
+    y = impl.gated_residual(x, br, a, 2)
+    for t in range(4):
+        for h in range(2):
+            for i in range(3):
+                c = h * 3 + i
+                assert abs(y[t, c] - (x[t, c] + a[t // 2, c] * br[t, h, i])) < 1e-15
+
+
+def pin_euler_dt0(impl):
+    r = _rng(24)
+    z = r.standard_normal((5, 64))
+    u = r.standard_normal((5, 64))
+    assert np.array_equal(impl.euler_step(z, u, np.zeros(5), 1), z)
+
+
+def pin_euler_exact_landing(impl):
+    r = _rng(25)
+    step = 1.0 / 16.0
+    x0 = r.integers(-64, 65, size=(8, 64)) * step
+    x1 = r.integers(-64, 65, size=(8, 64)) * step
+    # the page's straight path: x_t at t = 0 is the noise, its velocity is x1 - x0
+    assert np.array_equal(impl.interpolant(x0, x1, np.zeros(8)), x0)
+    assert np.array_equal(impl.interpolant(x0, x1, np.ones(8)), x1)
+    u = impl.velocity(x0, x1)
+    assert np.array_equal(impl.euler_step(x0, u, np.ones(8), 1), x1)
+
+
+def pin_euler_per_frame(impl):
+    r = _rng(26)
+    x0 = r.standard_normal((12, 64))
+    x1 = r.standard_normal((12, 64))
+    t = r.random(4)  # 4 frames of 3 tokens
+    xt = impl.interpolant(x0, x1, np.repeat(t, 3))
+    y = impl.euler_step(xt, impl.velocity(x0, x1), 1.0 - t, 3)
+    assert np.allclose(y, x1, rtol=0, atol=1e-12)
+    # a direction check: a small step moves toward x1 along the path
+    xs = impl.euler_step(xt, impl.velocity(x0, x1), np.full(4, 0.01), 3)
+    assert np.allclose(xs, impl.interpolant(x0, x1, np.repeat(t + 0.01, 3)), atol=1e-12)
+
+
+def pin_euler_30_steps(impl):
+    r = _rng(27)
+    x0 = r.standard_normal((3, 64))
+    x1 = r.standard_normal((3, 64))
+    u = impl.velocity(x0, x1)
+    z = x0.copy()
+    for _ in range(30):
+        z = impl.euler_step(z, u, np.full(3, 1.0 / 30.0), 1)
+    assert np.allclose(z, x1, rtol=0, atol=1e-12)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,142 @@
+"""Plant plausible mistakes in copies of the oracle (CPU only) and check that
+the pins catch every one: evidence that the pins constrain each function."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle_pins as P
+from oracle import attention as o_attn
+from oracle import rope as o_rope
+
+
+def _ln_unbiased(x, eps):
+    x = np.asarray(x, dtype=np.float64)
+    xc = x - x.mean(axis=-1, keepdims=True)
+    return xc / np.sqrt(xc.var(axis=-1, ddof=1, keepdims=True) + eps)
+
+
+def _ln_eps_outside(x, eps):
+    x = np.asarray(x, dtype=np.float64)
+    xc = x - x.mean(axis=-1, keepdims=True)
+    return xc / (np.sqrt((xc * xc).mean(axis=-1, keepdims=True)) + eps)
+
+
+def _mod_with(ln, one_plus=False, row_mod=False):
+    def f(x, gamma, beta, tpr, eps):
+        x = np.asarray(x, dtype=np.float64)
+        n = x.shape[0]
+        rows = (np.arange(n) % len(gamma)) if row_mod else (np.arange(n) // tpr)
+        g = np.asarray(gamma)[rows]
+        return ((1.0 + g) if one_plus else g) * ln(x, eps) + np.asarray(beta)[rows]
+    return f
+
+
+def _rope_with(sign=1.0, freq_dim=None, axis_perm=(0, 1, 2), half_split=False):
+    def f(x, pos, split, base):
+        x = np.asarray(x, dtype=np.float64)
+        pos = np.asarray(pos, dtype=np.float64)[:, list(axis_perm)]
+        hd = x.shape[-1]
+        table = []
+        off = 0
+        for a, d_a in enumerate(split):
+            for j in range(d_a // 2):
+                dd = freq_dim if freq_dim else d_a
+                table.append((a, off + 2 * j, float(base) ** (-2.0 * j / dd)))
+            off += d_a
+        ax = np.array([t[0] for t in table])
+        th = np.array([t[2] for t in table])
+        phi = pos[:, ax] * th
+        c, s = np.cos(phi)[:, None, :], sign * np.sin(phi)[:, None, :]
+        if half_split:
+            i0, i1 = np.arange(hd // 2), np.arange(hd // 2, hd)
+        else:
+            i0, i1 = np.arange(0, hd, 2), np.arange(1, hd, 2)
+        out = np.empty_like(x)
+        out[..., i0] = x[..., i0] * c - x[..., i1] * s
+        out[..., i1] = x[..., i0] * s + x[..., i1] * c
+        return out
+    return f
+
+
+def _attn_with(scale_pow=0.5, use_k_as_v=False, ignore_cu=False, transpose_scores=False):
+    def f(q, k, v, cu, rows=None, row_block=1024):
+        q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+        n, h, d = q.shape
+        cu = [0, n] if ignore_cu else list(cu)
+        out = np.zeros_like(q)
+        for s in range(len(cu) - 1):
+            lo, hi = cu[s], cu[s + 1]
+            for hh in range(h):
+                S = q[lo:hi, hh] @ k[lo:hi, hh].T / d ** scale_pow
+                if transpose_scores:
+                    S = S.T
+                P_ = o_attn.softmax_rows(S)
+                out[lo:hi, hh] = P_ @ (k if use_k_as_v else v)[lo:hi, hh]
+        return out if rows is None else out[np.asarray(rows)]
+    return f
+
+
+def _coords_swapped(n, gh, gw):
+    n = np.asarray(n, dtype=np.int64)
+    return np.stack([n // (gh * gw), n % gw, (n // gw) % gh], axis=-1)
+
+
+def _interp_reversed(x0, x1, t):
+    t = np.asarray(t, dtype=np.float64)
+    t = t[:, None] if t.ndim == 1 else t
+    return t * np.asarray(x0, np.float64) + (1 - t) * np.asarray(x1, np.float64)
+
+
+def _euler_minus(z, u, dt, tpr):
+    rows = np.arange(len(z)) // tpr
+    return np.asarray(z, np.float64) - np.asarray(dt, np.float64)[rows][:, None] * u
+
+
+def _residual_rowmod(x, br, a, tpr):
+    x = np.asarray(x, np.float64)
+    rows = np.arange(len(x)) % len(a)
+    return x + np.asarray(a)[rows] * np.asarray(br).reshape(x.shape)
+
+
+def _residual_unmerged(x, br, a, tpr):
+    x = np.asarray(x, np.float64)
+    b = np.asarray(br).transpose(0, 2, 1).reshape(x.shape)  # wrong head merge
+    rows = np.arange(len(x)) // tpr
+    return x + np.asarray(a)[rows] * b
+
+
+MUTANTS = {
+    "ln_unbiased_variance": dict(adaln_modulate=_mod_with(_ln_unbiased), layer_norm=_ln_unbiased),
+    "ln_eps_outside_sqrt": dict(adaln_modulate=_mod_with(_ln_eps_outside), layer_norm=_ln_eps_outside),
+    "modulate_one_plus_gamma": dict(adaln_modulate=_mod_with(P.real_impl().layer_norm, one_plus=True)),
+    "modulate_wrong_row": dict(adaln_modulate=_mod_with(P.real_impl().layer_norm, row_mod=True)),
+    "rope_negative_angle": dict(apply_rope=_rope_with(sign=-1.0)),
+    "rope_freq_over_head_dim": dict(apply_rope=_rope_with(freq_dim=64)),
+    "rope_axes_reversed": dict(apply_rope=_rope_with(axis_perm=(2, 1, 0))),
+    "rope_half_split_pairs": dict(apply_rope=_rope_with(half_split=True)),
+    "attn_scale_over_d": dict(attention=_attn_with(scale_pow=1.0)),
+    "attn_no_scale": dict(attention=_attn_with(scale_pow=0.0)),
+    "attn_k_as_v": dict(attention=_attn_with(use_k_as_v=True)),
+    "attn_across_sequences": dict(attention=_attn_with(ignore_cu=True)),
+    "attn_transposed_scores": dict(attention=_attn_with(transpose_scores=True)),
+    "grid_h_w_swapped": dict(coords=_coords_swapped),
+    "interpolant_reversed": dict(interpolant=_interp_reversed),
+    "euler_wrong_sign": dict(euler_step=_euler_minus),
+    "residual_wrong_row": dict(gated_residual=_residual_rowmod),
+    "residual_wrong_head_merge": dict(gated_residual=_residual_unmerged),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    impl = P.real_impl()
+    for k, v in MUTANTS[name].items():
+        setattr(impl, k, v)
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(impl)
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught mutant {name}"
