@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Throughput of the DiT attention-block hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  dit_adaln_modulate (x -> y), dit_rope3d (q, k in place), dit_attn3d (q, k, v -> o),
+  dit_gated_residual fused with the rectified-flow Euler update (x + alpha*o, z + dt*u).
+Inputs are seeded synthetic tensors shaped like the pages' image latent (default:
+128x128x16 latent, patch 2x2 -> 4096 tokens, batch 2, 24 heads x 128), resident in
+HBM before timing starts.
+
+Prints ONE JSON line. value = attention FLOPs per step / wall time per step
+(whole path), in TFLOP/s. roofline = the attention kernel's own rate, timed with
+HIP events around each of its launches on the stream it runs on, against the
+2.5 PFLOP/s dense bf16 MFMA peak. cpu_baseline = the float64 numpy oracle on a
+bounded sample of the same workload, scaled to the whole step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+WORKLOAD_KEYS = {"c1": "c1_tiny_f32", "c2": "c2_image_4096_bf16", "c3": "c3_video480p_32760_bf16",
+                 "c4": "c4_video720p_27280_bf16", "c5": "c5_varlen_frames_bf16"}
+ATTN_SRC = os.path.join(ROOT, "diffusion_transformer_video_amd", "csrc", "k_attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_KEYS))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="approximate CPU time budget of the oracle sample")
+    return p.parse_args()
+
+
+def source_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(workload):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs, or
+    None if there are none for this workload or the kernel changed since."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("source_sha") != source_sha(ATTN_SRC):
+        return None
+    return e.get("traffic_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(sharding is a design note only); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import diffusion_transformer_video_amd as dit
+    import synth
+
+    w = synth.WORKLOADS[WORKLOAD_KEYS[args.workload]]
+    torch.cuda.set_device(0)
+    dit.lib()
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    esz = 2 if w.dtype == "bf16" else 4
+
+    inp = synth.make(w, ["x", "gamma", "beta", "alpha", "q", "k", "v", "z", "u", "dt"])
+    d = lambda a, t=tdt: torch.from_numpy(np.ascontiguousarray(a)).to(t).cuda()
+    x, q, k, v, z, u = (d(inp[n]) for n in ("x", "q", "k", "v", "z", "u"))
+    g, b, al, dtr = (d(inp[n], torch.float32) for n in ("gamma", "beta", "alpha", "dt"))
+    cu = None if w.dense else torch.from_numpy(w.cu_seqlens).cuda()
+    y, o = torch.empty_like(x), torch.empty_like(q)
+    x_out, z_out = torch.empty_like(x), torch.empty_like(z)
+    o2d = o.view(w.tokens, w.d_model)
+    grid = (w.frames[0], *w.grid_hw)
+    del inp
+
+    names = ("modulate", "rope", "attn", "residual_euler")
+    ev = {n: [] for n in names}
+
+    def step(record):
+        def timed(name, fn):
+            if record:
+                a, bb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                bb.record()
+                ev[name].append((a, bb))
+            else:
+                fn()
+        timed("modulate", lambda: dit.dit_adaln_modulate(y, x, g, b, w.tokens_per_row, w.eps))
+        timed("rope", lambda: dit.dit_rope3d(q, k, grid, w.rope_split, w.rope_base, cu_seqlens=cu,
+                                             num_seqs=w.num_seqs))
+        if cu is None:
+            timed("attn", lambda: dit.dit_attn3d(o, q, k, v, num_seqs=w.num_seqs))
+        else:
+            timed("attn", lambda: dit.dit_attn3d(o, q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen))
+        timed("residual_euler", lambda: dit.dit_gated_residual(
+            x_out, x, o2d, al, w.tokens_per_row, euler=(z_out, z, u, dtr, w.tokens_per_row)))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    # whole-step wall time: plain events around the K steps (no per-kernel events)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step(False)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # per-kernel durations: events around each launch, on the launch stream
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    kern_ms = {n: float(np.mean([a.elapsed_time(bb) for a, bb in ev[n]])) for n in names}
+
+    flops = w.attn_flops()
+    tok, D, P = w.tokens, w.d_model, synth.LATENT_CHANNELS
+    algo_bytes = {
+        "modulate": 2 * tok * D * esz,
+        "rope": 4 * tok * D * esz,
+        "residual_euler": 3 * tok * D * esz + 3 * tok * P * esz,
+    }
+    attn_s = kern_ms["attn"] * 1e-3
+    achieved = flops / attn_s / 1e12
+    traffic = traffic_for(w.name)
+    kernels = {"attn": {"us": round(kern_ms["attn"] * 1e3, 2), "tflops": round(achieved, 2)}}
+    for n, nb in algo_bytes.items():
+        gbs = nb / (kern_ms[n] * 1e-3) / 1e9
+        kernels[n] = {"us": round(kern_ms[n] * 1e3, 2), "gbs": round(gbs, 1),
+                      "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nb}
+
+    out = {
+        "metric": "3D-attention TFLOP/s (fwd, bf16) at 1 MI355X and % of MFMA peak",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.1) adaLN parameters)",
+        "config": {"workload": w.name, "tokens": tok, "batch": w.num_seqs, "seq_len": w.max_seqlen,
+                   "seqlens": list(w.seqlens), "heads": w.heads, "head_dim": w.head_dim,
+                   "d_model": D, "latent_channels": P, "grid_thw": [w.frames[0], *w.grid_hw],
+                   "rope_split": list(w.rope_split), "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "attn_bf16_kernel<128,4>",
+                     "flops_per_launch": flops},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, budget_s):
+    """The float64 oracle on a bounded sample: whole (sequence, head) attention
+    problems plus the elementwise steps on the same share of tokens, scaled up
+    by the share to one whole step."""
+    import numpy as np
+
+    import synth
+    from oracle import attention as o_attn
+    from oracle import epilogue as o_epi
+    from oracle import grid as o_grid
+    from oracle import modulate as o_mod
+    from oracle import rope as o_rope
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    print(f"[bench] cpu baseline: oracle on up to ~{budget_s:.0f}s of work", file=sys.stderr, flush=True)
+    inp = synth.make(w, ["q", "k", "v"])
+    cu = w.cu_seqlens
+    total_pairs = w.num_seqs * w.heads
+    t_attn, pairs_done = 0.0, 0
+    while pairs_done < total_pairs and (pairs_done == 0 or t_attn < 0.8 * budget_s):
+        s, h = divmod(pairs_done, w.heads)
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        sl = slice(lo, hi)
+        t = time.perf_counter()
+        o_attn.attention(inp["q"][sl, h:h + 1], inp["k"][sl, h:h + 1], inp["v"][sl, h:h + 1], [0, hi - lo])
+        t_attn += time.perf_counter() - t
+        pairs_done += 1
+    # share of the step's attention flops covered by the sample
+    done_flops = sum(4 * (int(cu[p // w.heads + 1]) - int(cu[p // w.heads])) ** 2 * w.head_dim
+                     for p in range(pairs_done))
+    share = done_flops / w.attn_flops()
+    rows = max(1, int(round(share * w.tokens)))
+    e = synth.make(w, ["x", "gamma", "beta", "alpha", "z", "u", "dt"])
+    pos = o_grid.positions(w.cu_seqlens, *w.grid_hw)[:rows]
+    t = time.perf_counter()
+    o_mod.adaln_modulate(e["x"][:rows], e["gamma"], e["beta"], w.tokens_per_row, w.eps)
+    o_rope.apply_rope(inp["q"][:rows], pos, w.rope_split, w.rope_base)
+    o_rope.apply_rope(inp["k"][:rows], pos, w.rope_split, w.rope_base)
+    o_epi.gated_residual(e["x"][:rows], inp["v"][:rows], e["alpha"], w.tokens_per_row)
+    o_epi.euler_step(e["z"][:rows], e["u"][:rows], e["dt"], w.tokens_per_row)
+    t_elem = time.perf_counter() - t
+    step_s = (t_attn + t_elem) / share
+    return {"value": round(w.attn_flops() / step_s / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"float64 numpy oracle: attention for {pairs_done} of {total_pairs} "
+                       f"(sequence, head) pairs plus modulate/RoPE/residual/Euler on "
+                       f"the same share ({rows} of {w.tokens} tokens); {t_attn + t_elem:.1f} s measured, "
+                       f"scaled by {1 / share:.1f}x to one step ({step_s:.1f} s)")}
+
+
+if __name__ == "__main__":
+    main()

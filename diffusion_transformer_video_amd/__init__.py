@@ -1,0 +1,199 @@
+"""Python binding of libdit (include/dit.h): the DiT attention-block hot path
+on MI355X (gfx950).
+
+Argument marshalling only. Each function takes torch tensors that already live
+on the GPU, checks dtype/shape/contiguity, and calls the C entry point of the
+same name on torch's current stream; every step runs in the HIP kernels. There
+is no fallback: if libdit.so is missing or the device is not gfx950 the call
+raises.
+
+Layout: activations are token-major and contiguous -- hidden [tokens, d_model],
+q/k/v/o [tokens, heads, head_dim], latent [tokens, channels]; parameter tables
+gamma/beta/alpha [rows, d_model] and dt_rows [rows] are float32 with
+row = token // tokens_per_row.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdit.so")
+
+DIT_F32, DIT_BF16 = 0, 1
+DIT_OK, DIT_E_INVAL, DIT_E_UNSUPPORTED, DIT_E_HIP = 0, 1, 2, 3
+
+EXPORTS = ("dit_last_error", "dit_version", "dit_adaln_modulate", "dit_rope3d",
+           "dit_attn3d", "dit_gated_residual", "rf_euler_step")
+
+
+class DitError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class EulerArgs(ctypes.Structure):
+    _fields_ = [("z_out", ctypes.c_void_p), ("z", ctypes.c_void_p), ("u", ctypes.c_void_p),
+                ("dt_rows", ctypes.c_void_p), ("tokens", ctypes.c_int64),
+                ("channels", ctypes.c_int32), ("tokens_per_row", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdit.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -m diffusion_transformer_video_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        L.dit_last_error.restype = ctypes.c_char_p
+        L.dit_last_error.argtypes = []
+        L.dit_version.restype = ctypes.c_int
+        L.dit_version.argtypes = []
+        L.dit_adaln_modulate.restype = ctypes.c_int
+        L.dit_adaln_modulate.argtypes = [vp, vp, vp, vp, i64, i32, i64, f32, i32, vp]
+        L.dit_rope3d.restype = ctypes.c_int
+        L.dit_rope3d.argtypes = [vp, vp, i64, i32, i32, i32, i32, i32, vp, i32,
+                                 i32, i32, i32, f32, vp, i32, vp]
+        L.dit_attn3d.restype = ctypes.c_int
+        L.dit_attn3d.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, vp]
+        L.dit_gated_residual.restype = ctypes.c_int
+        L.dit_gated_residual.argtypes = [vp, vp, vp, vp, i64, i32, i64,
+                                         ctypes.POINTER(EulerArgs), i32, vp]
+        L.rf_euler_step.restype = ctypes.c_int
+        L.rf_euler_step.argtypes = [vp, vp, vp, vp, i64, i32, i64, i32, vp]
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != DIT_OK:
+        raise DitError(rc, lib().dit_last_error().decode(errors="replace"))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DIT_BF16
+    if t.dtype == torch.float32:
+        return DIT_F32
+    raise TypeError(f"activations must be bfloat16 or float32, got {t.dtype}")
+
+
+def _dev(*ts) -> None:
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _f32(*ts) -> None:
+    torch = _torch()
+    for t in ts:
+        if t.dtype != torch.float32:
+            raise TypeError("parameter tables (gamma, beta, alpha, dt_rows) must be float32")
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def dit_adaln_modulate(y, x, gamma, beta, tokens_per_row: int, eps: float = 1e-6, stream=None):
+    """y = gamma[row] * LayerNorm(x) + beta[row]; x, y [tokens, d_model]."""
+    _dev(y, x, gamma, beta)
+    _f32(gamma, beta)
+    if x.dim() != 2 or y.shape != x.shape or x.dtype != y.dtype:
+        raise ValueError("x and y must be [tokens, d_model] of one dtype")
+    tokens, d = x.shape
+    _check(lib().dit_adaln_modulate(_ptr(y), _ptr(x), _ptr(gamma), _ptr(beta), tokens, d,
+                                    int(tokens_per_row), float(eps), _dtype_code(x), _stream(stream)))
+    return y
+
+
+def dit_rope3d(q, k, grid: Sequence[int], split: Sequence[int], base: float = 10000.0,
+               cu_seqlens=None, num_seqs: int = 1, pos_out=None, stream=None):
+    """Rotate q and k ([tokens, heads, head_dim]) in place by R_3D(t', h', w').
+
+    grid = (T', H', W'); with cu_seqlens, T' is ignored and positions restart per
+    packed sequence. split = (d_t, d_h, d_w)."""
+    _dev(q, k, cu_seqlens, pos_out)
+    if q.dim() != 3 or (k is not None and (k.shape != q.shape or k.dtype != q.dtype)):
+        raise ValueError("q and k must be [tokens, heads, head_dim] of one dtype")
+    tokens, heads, hd = q.shape
+    if cu_seqlens is not None:
+        num_seqs = cu_seqlens.numel() - 1
+    _check(lib().dit_rope3d(_ptr(q), _ptr(k), tokens, heads, hd, int(grid[0]), int(grid[1]),
+                            int(grid[2]), _ptr(cu_seqlens), int(num_seqs), int(split[0]),
+                            int(split[1]), int(split[2]), float(base), _ptr(pos_out),
+                            _dtype_code(q), _stream(stream)))
+    return q, k
+
+
+def dit_attn3d(o, q, k, v, cu_seqlens=None, num_seqs: int = 1, max_seqlen: int = 0, stream=None):
+    """o = softmax(q k^T / sqrt(head_dim)) v per (sequence, head); all [tokens, heads, hd]."""
+    _dev(o, q, k, v, cu_seqlens)
+    if q.dim() != 3 or any(t.shape != q.shape or t.dtype != q.dtype for t in (k, v, o)):
+        raise ValueError("o, q, k, v must be [tokens, heads, head_dim] of one dtype")
+    tokens, heads, hd = q.shape
+    if cu_seqlens is not None:
+        num_seqs = cu_seqlens.numel() - 1
+    _check(lib().dit_attn3d(_ptr(o), _ptr(q), _ptr(k), _ptr(v), tokens, heads, hd,
+                            _ptr(cu_seqlens), int(num_seqs), int(max_seqlen), _dtype_code(q),
+                            _stream(stream)))
+    return o
+
+
+def dit_gated_residual(x_out, x, branch, alpha, tokens_per_row: int, euler=None, stream=None):
+    """x_out = x + alpha[row] * branch (branch heads merged); optional fused Euler
+    pass: euler = (z_out, z, u, dt_rows, tokens_per_row)."""
+    _dev(x_out, x, branch, alpha)
+    _f32(alpha)
+    if x.dim() != 2 or x_out.shape != x.shape or branch.numel() != x.numel():
+        raise ValueError("x, x_out must be [tokens, d_model] and branch the same size")
+    if branch.dtype != x.dtype or x_out.dtype != x.dtype:
+        raise ValueError("x, x_out and branch must share one dtype")
+    tokens, d = x.shape
+    ea = None
+    if euler is not None:
+        z_out, z, u, dt_rows, tpr = euler
+        _dev(z_out, z, u, dt_rows)
+        _f32(dt_rows)
+        if z.dim() != 2 or z_out.shape != z.shape or u.shape != z.shape or z.dtype != x.dtype:
+            raise ValueError("Euler tensors must be [tokens, channels] in the residual's dtype")
+        ea = EulerArgs(_ptr(z_out), _ptr(z), _ptr(u), _ptr(dt_rows), z.shape[0], z.shape[1], int(tpr))
+    _check(lib().dit_gated_residual(_ptr(x_out), _ptr(x), _ptr(branch), _ptr(alpha), tokens, d,
+                                    int(tokens_per_row), ctypes.byref(ea) if ea is not None else None,
+                                    _dtype_code(x), _stream(stream)))
+    return x_out
+
+
+def rf_euler_step(z_out, z, u, dt_rows, tokens_per_row: int, stream=None):
+    """z_out = z + dt_rows[row] * u; z, u [tokens, channels]."""
+    _dev(z_out, z, u, dt_rows)
+    _f32(dt_rows)
+    if z.dim() != 2 or z_out.shape != z.shape or u.shape != z.shape or u.dtype != z.dtype:
+        raise ValueError("z, z_out, u must be [tokens, channels] of one dtype")
+    tokens, ch = z.shape
+    _check(lib().rf_euler_step(_ptr(z_out), _ptr(z), _ptr(u), _ptr(dt_rows), tokens, ch,
+                               int(tokens_per_row), _dtype_code(z), _stream(stream)))
+    return z_out

@@ -1,0 +1,251 @@
+// C-ABI entry points (include/dit.h): argument validation, device check and
+// dispatch to the gfx950 kernels. Validation is plain host code and runs before
+// any HIP call, so a rejected call launches nothing and writes nothing, even on
+// a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/dit.h"
+#include "dit_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return DIT_OK;
+}
+
+int elem_size(int32_t dtype) { return dtype == DIT_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap (byte ranges)
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+int check_dtype(int32_t dtype, const char* fn) {
+    if (dtype != DIT_F32 && dtype != DIT_BF16)
+        return fail(DIT_E_UNSUPPORTED, "%s: unknown dtype %d (expected DIT_F32=0 or DIT_BF16=1)", fn, dtype);
+    return DIT_OK;
+}
+
+// Device check, cached per device: the kernels are built for gfx950 only.
+std::atomic<int> g_dev_state[64];   // 0 unknown, 1 gfx950, 2 other
+
+int check_device(const char* fn) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DIT_E_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(DIT_E_UNSUPPORTED, "%s: device ordinal %d out of range", fn, dev);
+    int st = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(DIT_E_HIP, "%s: hipGetDeviceProperties: %s", fn, hipGetErrorString(e));
+        st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_dev_state[dev].store(st, std::memory_order_relaxed);
+        if (st == 2)
+            return fail(DIT_E_UNSUPPORTED, "%s: device %d is %s; this library is built for gfx950 only",
+                        fn, dev, prop.gcnArchName);
+    }
+    if (st == 2) return fail(DIT_E_UNSUPPORTED, "%s: device %d is not gfx950", fn, dev);
+    return DIT_OK;
+}
+
+int launched(hipError_t e, const char* fn) {
+    if (e != hipSuccess) return fail(DIT_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+int validate_rows(const char* fn, int64_t tokens, int64_t tokens_per_row) {
+    if (tokens <= 0) return fail(DIT_E_INVAL, "%s: tokens must be > 0 (got %lld)", fn, (long long)tokens);
+    if (tokens_per_row <= 0 || tokens % tokens_per_row != 0)
+        return fail(DIT_E_INVAL, "%s: tokens (%lld) must be a positive multiple of tokens_per_row (%lld)",
+                    fn, (long long)tokens, (long long)tokens_per_row);
+    return DIT_OK;
+}
+
+int validate_euler(const char* fn, void* z_out, const void* z, const void* u, const float* dt_rows,
+                   int64_t tokens, int32_t channels, int64_t tokens_per_row, int32_t dtype) {
+    if (!z_out || !z || !u || !dt_rows) return fail(DIT_E_INVAL, "%s: NULL pointer argument", fn);
+    int rc = validate_rows(fn, tokens, tokens_per_row);
+    if (rc) return rc;
+    if (channels <= 0) return fail(DIT_E_INVAL, "%s: channels must be > 0", fn);
+    if (channels % 8 != 0)
+        return fail(DIT_E_UNSUPPORTED, "%s: channels (%d) must be a multiple of 8", fn, channels);
+    if (!aligned16(z_out) || !aligned16(z) || !aligned16(u) || !aligned16(dt_rows))
+        return fail(DIT_E_UNSUPPORTED, "%s: tensors must be 16-byte aligned", fn);
+    const int64_t bytes = tokens * channels * elem_size(dtype);
+    if (z_out != z && overlaps(z_out, bytes, z, bytes))
+        return fail(DIT_E_INVAL, "%s: z_out partially overlaps z", fn);
+    if (overlaps(z_out, bytes, u, bytes)) return fail(DIT_E_INVAL, "%s: z_out overlaps u", fn);
+    return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dit_last_error(void) { return g_err.c_str(); }
+
+int dit_version(void) { return 10000; }
+
+int dit_adaln_modulate(void* y, const void* x, const float* gamma, const float* beta,
+                       int64_t tokens, int32_t d_model, int64_t tokens_per_row,
+                       float eps, int32_t dtype, void* stream) {
+    const char* fn = "dit_adaln_modulate";
+    if (int rc = check_dtype(dtype, fn)) return rc;
+    if (!y || !x || !gamma || !beta) return fail(DIT_E_INVAL, "%s: NULL pointer argument", fn);
+    if (int rc = validate_rows(fn, tokens, tokens_per_row)) return rc;
+    if (!(eps > 0.f) || !std::isfinite(eps)) return fail(DIT_E_INVAL, "%s: eps must be finite and > 0", fn);
+    if (d_model <= 0) return fail(DIT_E_INVAL, "%s: d_model must be > 0", fn);
+    if (d_model % 8 != 0 || d_model > 8192)
+        return fail(DIT_E_UNSUPPORTED, "%s: d_model (%d) must be a multiple of 8 and <= 8192", fn, d_model);
+    if (!aligned16(y) || !aligned16(x) || !aligned16(gamma) || !aligned16(beta))
+        return fail(DIT_E_UNSUPPORTED, "%s: tensors must be 16-byte aligned", fn);
+    const int64_t bytes = tokens * d_model * elem_size(dtype);
+    if (y != x && overlaps(y, bytes, x, bytes)) return fail(DIT_E_INVAL, "%s: y partially overlaps x", fn);
+    if (int rc = check_device(fn)) return rc;
+    dit::ModulateArgs a{y, x, gamma, beta, tokens, d_model, tokens_per_row, eps};
+    return launched(dit::launch_adaln_modulate(a, dtype == DIT_BF16, (hipStream_t)stream), fn);
+}
+
+int dit_rope3d(void* q, void* k, int64_t tokens, int32_t heads, int32_t head_dim,
+               int32_t grid_t, int32_t grid_h, int32_t grid_w,
+               const int32_t* cu_seqlens, int32_t num_seqs,
+               int32_t d_t, int32_t d_h, int32_t d_w, float base,
+               int32_t* pos_out, int32_t dtype, void* stream) {
+    const char* fn = "dit_rope3d";
+    if (int rc = check_dtype(dtype, fn)) return rc;
+    if (!q) return fail(DIT_E_INVAL, "%s: q is NULL", fn);
+    if (tokens <= 0) return fail(DIT_E_INVAL, "%s: tokens must be > 0", fn);
+    if (heads <= 0 || head_dim <= 0) return fail(DIT_E_INVAL, "%s: heads and head_dim must be > 0", fn);
+    if (d_t < 0 || d_h < 0 || d_w < 0 || (d_t | d_h | d_w) & 1)
+        return fail(DIT_E_INVAL, "%s: d_t, d_h, d_w must be even and >= 0 (got %d/%d/%d)", fn, d_t, d_h, d_w);
+    if (d_t + d_h + d_w != head_dim)
+        return fail(DIT_E_INVAL, "%s: d_t + d_h + d_w (%d) must equal head_dim (%d)", fn, d_t + d_h + d_w, head_dim);
+    if (!(base > 1.f) || !std::isfinite(base)) return fail(DIT_E_INVAL, "%s: base must be finite and > 1", fn);
+    if (grid_h <= 0 || grid_w <= 0) return fail(DIT_E_INVAL, "%s: grid_h and grid_w must be > 0", fn);
+    if (num_seqs <= 0) return fail(DIT_E_INVAL, "%s: num_seqs must be > 0", fn);
+    if (cu_seqlens == nullptr) {
+        if (grid_t <= 0) return fail(DIT_E_INVAL, "%s: grid_t must be > 0 in dense mode", fn);
+        const int64_t L = (int64_t)grid_t * grid_h * grid_w;
+        if (tokens != (int64_t)num_seqs * L)
+            return fail(DIT_E_INVAL, "%s: dense tokens (%lld) != num_seqs * grid_t * grid_h * grid_w (%lld)",
+                        fn, (long long)tokens, (long long)num_seqs * L);
+    }
+    if (head_dim % 8 != 0 || head_dim > 256 || (64 % (head_dim / 8)) != 0)
+        return fail(DIT_E_UNSUPPORTED, "%s: head_dim (%d) must be one of 8, 16, 32, 64, 128, 256", fn, head_dim);
+    if (!aligned16(q) || (k && !aligned16(k)))
+        return fail(DIT_E_UNSUPPORTED, "%s: q and k must be 16-byte aligned", fn);
+    const int64_t bytes = tokens * heads * head_dim * elem_size(dtype);
+    if (k && overlaps(q, bytes, k, bytes)) return fail(DIT_E_INVAL, "%s: q and k overlap", fn);
+    if (int rc = check_device(fn)) return rc;
+    dit::RopeArgs a{q, k, tokens, heads, head_dim, grid_t, grid_h, grid_w, cu_seqlens, num_seqs,
+                    d_t, d_h, d_w, std::log2(base), pos_out};
+    return launched(dit::launch_rope3d(a, dtype == DIT_BF16, (hipStream_t)stream), fn);
+}
+
+int dit_attn3d(void* o, const void* q, const void* k, const void* v,
+               int64_t tokens, int32_t heads, int32_t head_dim,
+               const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+               int32_t dtype, void* stream) {
+    const char* fn = "dit_attn3d";
+    if (int rc = check_dtype(dtype, fn)) return rc;
+    if (!o || !q || !k || !v) return fail(DIT_E_INVAL, "%s: NULL pointer argument", fn);
+    if (tokens <= 0) return fail(DIT_E_INVAL, "%s: tokens must be > 0", fn);
+    if (heads <= 0) return fail(DIT_E_INVAL, "%s: heads must be > 0", fn);
+    if (num_seqs <= 0) return fail(DIT_E_INVAL, "%s: num_seqs must be > 0", fn);
+    int32_t seqlen = max_seqlen;
+    if (cu_seqlens == nullptr) {
+        if (tokens % num_seqs != 0)
+            return fail(DIT_E_INVAL, "%s: dense tokens (%lld) must be a multiple of num_seqs (%d)",
+                        fn, (long long)tokens, num_seqs);
+        if (tokens / num_seqs > 0x7fffffff) return fail(DIT_E_UNSUPPORTED, "%s: sequence too long", fn);
+        seqlen = (int32_t)(tokens / num_seqs);
+    } else if (max_seqlen <= 0 || max_seqlen > tokens) {
+        return fail(DIT_E_INVAL, "%s: packed mode needs 0 < max_seqlen <= tokens (got %d)", fn, max_seqlen);
+    }
+    if (head_dim != 64 && head_dim != 128)
+        return fail(DIT_E_UNSUPPORTED, "%s: head_dim must be 64 or 128 (got %d)", fn, head_dim);
+    if (!aligned16(o) || !aligned16(q) || !aligned16(k) || !aligned16(v))
+        return fail(DIT_E_UNSUPPORTED, "%s: tensors must be 16-byte aligned", fn);
+    const int64_t bytes = tokens * heads * head_dim * elem_size(dtype);
+    if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
+        return fail(DIT_E_INVAL, "%s: o must not overlap q, k or v", fn);
+    if (int rc = check_device(fn)) return rc;
+    dit::AttnArgs a{o, q, k, v, tokens, heads, head_dim, cu_seqlens, num_seqs, seqlen,
+                    (float)(1.4426950408889634 / std::sqrt((double)head_dim)),
+                    (float)(1.0 / std::sqrt((double)head_dim))};
+    hipError_t e = dtype == DIT_BF16 ? dit::launch_attn3d_bf16(a, (hipStream_t)stream)
+                                     : dit::launch_attn3d_f32(a, (hipStream_t)stream);
+    return launched(e, fn);
+}
+
+int dit_gated_residual(void* x_out, const void* x, const void* branch, const float* alpha,
+                       int64_t tokens, int32_t d_model, int64_t tokens_per_row,
+                       const dit_euler_args* euler, int32_t dtype, void* stream) {
+    const char* fn = "dit_gated_residual";
+    if (int rc = check_dtype(dtype, fn)) return rc;
+    if (!x_out || !x || !branch || !alpha) return fail(DIT_E_INVAL, "%s: NULL pointer argument", fn);
+    if (int rc = validate_rows(fn, tokens, tokens_per_row)) return rc;
+    if (d_model <= 0) return fail(DIT_E_INVAL, "%s: d_model must be > 0", fn);
+    if (d_model % 8 != 0) return fail(DIT_E_UNSUPPORTED, "%s: d_model (%d) must be a multiple of 8", fn, d_model);
+    if (!aligned16(x_out) || !aligned16(x) || !aligned16(branch) || !aligned16(alpha))
+        return fail(DIT_E_UNSUPPORTED, "%s: tensors must be 16-byte aligned", fn);
+    const int64_t bytes = tokens * d_model * elem_size(dtype);
+    if (x_out != x && overlaps(x_out, bytes, x, bytes))
+        return fail(DIT_E_INVAL, "%s: x_out partially overlaps x", fn);
+    if (overlaps(x_out, bytes, branch, bytes)) return fail(DIT_E_INVAL, "%s: x_out overlaps branch", fn);
+    dit::EulerArgs ea{};
+    if (euler) {
+        if (int rc = validate_euler("dit_gated_residual(euler)", euler->z_out, euler->z, euler->u,
+                                    euler->dt_rows, euler->tokens, euler->channels,
+                                    euler->tokens_per_row, dtype))
+            return rc;
+        const int64_t zb = euler->tokens * euler->channels * elem_size(dtype);
+        if (overlaps(euler->z_out, zb, x_out, bytes) || overlaps(euler->z_out, zb, x, bytes) ||
+            overlaps(euler->z_out, zb, branch, bytes) || overlaps(x_out, bytes, euler->z, zb) ||
+            overlaps(x_out, bytes, euler->u, zb))
+            return fail(DIT_E_INVAL, "%s: Euler tensors overlap the residual tensors", fn);
+        ea = dit::EulerArgs{euler->z_out, euler->z, euler->u, euler->dt_rows, euler->tokens,
+                            euler->channels, euler->tokens_per_row};
+    }
+    if (int rc = check_device(fn)) return rc;
+    dit::ResidualArgs ra{x_out, x, branch, alpha, tokens, d_model, tokens_per_row};
+    return launched(dit::launch_epilogue(&ra, euler ? &ea : nullptr, dtype == DIT_BF16, (hipStream_t)stream), fn);
+}
+
+int rf_euler_step(void* z_out, const void* z, const void* u, const float* dt_rows,
+                  int64_t tokens, int32_t channels, int64_t tokens_per_row,
+                  int32_t dtype, void* stream) {
+    const char* fn = "rf_euler_step";
+    if (int rc = check_dtype(dtype, fn)) return rc;
+    if (int rc = validate_euler(fn, z_out, z, u, dt_rows, tokens, channels, tokens_per_row, dtype)) return rc;
+    if (int rc = check_device(fn)) return rc;
+    dit::EulerArgs ea{z_out, z, u, dt_rows, tokens, channels, tokens_per_row};
+    return launched(dit::launch_epilogue(nullptr, &ea, dtype == DIT_BF16, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Internal launch interface between the C-ABI layer (dit_api.cpp) and the
+// kernel translation units. Every launcher assumes its arguments were validated
+// by the C-ABI layer and only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+struct ModulateArgs {
+    void* y; const void* x; const float* gamma; const float* beta;
+    int64_t tokens; int d_model; int64_t tokens_per_row; float eps;
+};
+hipError_t launch_adaln_modulate(const ModulateArgs& a, bool bf16, hipStream_t s);
+
+struct RopeArgs {
+    void* q; void* k; int64_t tokens; int heads; int head_dim;
+    int grid_t, grid_h, grid_w;
+    const int32_t* cu_seqlens; int num_seqs;
+    int d_t, d_h, d_w; float log2_base;
+    int32_t* pos_out;
+};
+hipError_t launch_rope3d(const RopeArgs& a, bool bf16, hipStream_t s);
+
+struct AttnArgs {
+    void* o; const void* q; const void* k; const void* v;
+    int64_t tokens; int heads; int head_dim;
+    const int32_t* cu_seqlens;   // NULL => dense
+    int num_seqs; int max_seqlen;   // dense: max_seqlen = tokens / num_seqs
+    float scale_log2;            // log2(e) / sqrt(head_dim)
+    float scale;                 // 1 / sqrt(head_dim)
+};
+hipError_t launch_attn3d_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn3d_f32(const AttnArgs& a, hipStream_t s);
+
+struct EulerArgs {
+    void* z_out; const void* z; const void* u; const float* dt_rows;
+    int64_t tokens; int channels; int64_t tokens_per_row;
+};
+struct ResidualArgs {
+    void* x_out; const void* x; const void* branch; const float* alpha;
+    int64_t tokens; int d_model; int64_t tokens_per_row;
+};
+// residual may have tokens == 0 (Euler only); euler may be NULL.
+hipError_t launch_epilogue(const ResidualArgs* r, const EulerArgs* e, bool bf16, hipStream_t s);
+
+}  // namespace dit

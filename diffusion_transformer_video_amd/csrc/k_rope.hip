@@ -1,0 +1,109 @@
+// 3D rotary position embedding, in place on q and k, for gfx950.
+//
+// "DiT, Flow Matching e 3D Attention", section "3D-RoPE e atencao
+// espaco-temporal": d_head = d_t + d_h + d_w; each slice turns coordinate pairs
+// by angles driven by its own grid coordinate (frame t', row h', column w'),
+// and the same rotation R_3D(t', h', w') is applied to q and k of every head.
+//
+// HBM-bound: q and k are each read and written once (8 bytes per bf16 element
+// of q when both are rotated). One wave owns one token: the integer
+// token -> (sequence, t', h', w') map is computed once per wave; each lane owns
+// one 8-value chunk of the head vector (4 pairs) and evaluates the 4 pair angles
+// once, then rotates that chunk in every head of q and k (64 / (head_dim/8)
+// heads per pass, so a pass is one contiguous, coalesced span of the token row).
+#include "dit_device.hpp"
+#include "dit_internal.h"
+
+namespace dit {
+namespace {
+
+constexpr int kWaves = 4;
+
+__device__ __forceinline__ void rotate8(float (&f)[8], const float (&cs)[4], const float (&sn)[4]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float x0 = f[2 * p], x1 = f[2 * p + 1];
+        f[2 * p] = x0 * cs[p] - x1 * sn[p];
+        f[2 * p + 1] = x0 * sn[p] + x1 * cs[p];
+    }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(64 * kWaves) void rope3d_kernel(RopeArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t tok = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (tok >= a.tokens) return;
+
+    // token -> position within its sequence
+    int64_t n;
+    if (a.cu_seqlens == nullptr) {
+        const int64_t L = (int64_t)a.grid_t * a.grid_h * a.grid_w;
+        n = tok % L;
+    } else {
+        int lo = 0, hi = a.num_seqs;  // largest s with cu[s] <= tok
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if ((int64_t)a.cu_seqlens[mid] <= tok) lo = mid; else hi = mid;
+        }
+        n = tok - (int64_t)a.cu_seqlens[lo];
+    }
+    const int64_t hw = (int64_t)a.grid_h * a.grid_w;
+    const int pt = (int)(n / hw);
+    const int ph = (int)((n / a.grid_w) % a.grid_h);
+    const int pw = (int)(n % a.grid_w);
+    if (a.pos_out != nullptr && lane == 0) {
+        a.pos_out[3 * tok + 0] = pt;
+        a.pos_out[3 * tok + 1] = ph;
+        a.pos_out[3 * tok + 2] = pw;
+    }
+
+    const int cph = a.head_dim >> 3;      // chunks per head (divides 64)
+    const int hpp = 64 / cph;             // heads per pass
+    const int c = lane % cph;
+    const int hsub = lane / cph;
+
+    float cs[4], sn[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int dim = 8 * c + 2 * p;
+        int pos, j, da;
+        if (dim < a.d_t) {
+            pos = pt; j = dim >> 1; da = a.d_t;
+        } else if (dim < a.d_t + a.d_h) {
+            pos = ph; j = (dim - a.d_t) >> 1; da = a.d_h;
+        } else {
+            pos = pw; j = (dim - a.d_t - a.d_h) >> 1; da = a.d_w;
+        }
+        const float theta = exp2f(-(float)(2 * j) / (float)da * a.log2_base);
+        sincosf((float)pos * theta, &sn[p], &cs[p]);
+    }
+
+    const int64_t tok_chunk = tok * (int64_t)a.heads * cph;
+    for (int h = hsub; h < a.heads; h += hpp) {
+        const int64_t idx = tok_chunk + (int64_t)h * cph + c;
+        float fq[8];
+        Vec8<BF16>::load(a.q, idx, fq);
+        if (a.k != nullptr) {
+            float fk[8];
+            Vec8<BF16>::load(a.k, idx, fk);
+            rotate8(fk, cs, sn);
+            Vec8<BF16>::store(a.k, idx, fk);
+        }
+        rotate8(fq, cs, sn);
+        Vec8<BF16>::store(a.q, idx, fq);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rope3d(const RopeArgs& a, bool bf16, hipStream_t s) {
+    const dim3 grid((unsigned)((a.tokens + kWaves - 1) / kWaves));
+    const dim3 block(64 * kWaves);
+    if (bf16)
+        hipLaunchKernelGGL(rope3d_kernel<true>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(rope3d_kernel<false>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace dit

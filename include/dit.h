@@ -1,0 +1,172 @@
+/*
+ * dit.h -- C-ABI of the DiT attention-block hot path for AMD Instinct MI355X (gfx950).
+ *
+ * One DiT block's attention half plus the sampler update:
+ *   dit_adaln_modulate   y  = gamma * LayerNorm(x) + beta            (adaLN-Zero)
+ *   dit_rope3d           q, k <- R_3D(t', h', w') q, k               (3D-RoPE)
+ *   dit_attn3d           o  = softmax(q k^T / sqrt(d_head)) v        (full 3D attention)
+ *   dit_gated_residual   x' = x + alpha * o   [+ fused Euler pass]   (gated residual)
+ *   rf_euler_step        z' = z + dt * u                             (rectified-flow Euler)
+ *
+ * Definitions come from the pages "DiT, Flow Matching e 3D Attention: A Engenharia
+ * de Video com IA" (sections "A ruptura da U-Net", "Flow Matching e Rectified Flow",
+ * "3D-RoPE e atencao espaco-temporal") and "Por que e absurdamente dificil gerar um
+ * filme inteiro usando IA" (section "Matematica por tras").
+ *
+ * Layout (every activation tensor is token-major and contiguous):
+ *   hidden x, y, branch      [tokens][d_model]
+ *   q, k, v, o               [tokens][heads][head_dim]   (== [tokens][d_model])
+ *   latent z, u              [tokens][channels]          (channels = C*p_t*p_h*p_w)
+ *   gamma, beta, alpha       [rows][d_model] float32, row = token / tokens_per_row
+ *   dt_rows                  [rows] float32
+ *   cu_seqlens               [num_seqs + 1] int32, offsets of packed sequences
+ * Tokens of one sequence are ordered time-major, w' fastest:
+ *   t' = n / (H'W'), h' = (n / W') % H', w' = n % W'   (n local to its sequence).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers to tensors are DEVICE pointers owned by the caller. The library
+ *     allocates no device memory and keeps no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue work
+ *     on it and never synchronise; results are visible after the stream is
+ *     synchronised. Faults inside a running kernel surface at that sync.
+ *   - `dtype` selects the activation storage: DIT_F32 or DIT_BF16. Parameters
+ *     (gamma, beta, alpha, dt_rows) are float32 in both cases. All arithmetic is
+ *     float32; each bf16 output is rounded once (round to nearest even).
+ *   - Return DIT_OK on success. On error nothing is launched, nothing is
+ *     written, and dit_last_error() describes the problem:
+ *       DIT_E_INVAL        bad argument (NULL pointer, size, split, overlap ...)
+ *       DIT_E_UNSUPPORTED  valid but unsupported (head_dim, alignment, device)
+ *       DIT_E_HIP          a HIP call failed (message from hipGetErrorString)
+ *     Arguments are validated before the device is queried, so argument errors
+ *     are reported even on a machine without a GPU.
+ *   - Device data is not inspected on the host: cu_seqlens must start at 0,
+ *     be non-decreasing and end at `tokens` (unchecked precondition).
+ */
+#ifndef DIT_H_
+#define DIT_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DIT_F32 = 0, DIT_BF16 = 1 } dit_dtype;
+
+enum { DIT_OK = 0, DIT_E_INVAL = 1, DIT_E_UNSUPPORTED = 2, DIT_E_HIP = 3 };
+
+/* Text of the last error on the calling thread ("" if none). Library-owned,
+ * valid until the next dit_* / rf_* call on this thread. */
+const char* dit_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int dit_version(void);
+
+/*
+ * adaLN-Zero modulation, "DiT, Flow Matching e 3D Attention", section "A ruptura
+ * da U-Net" (block equations: gamma_1 * LayerNorm(x_l) + beta_1 feeds attention):
+ *   y[tok][c] = gamma[row][c] * (x[tok][c] - mu) / sqrt(var + eps) + beta[row][c]
+ * with mu, var the mean and biased variance of x[tok][:], row = tok / tokens_per_row.
+ *
+ *   y, x            [tokens][d_model] activations (dtype); y == x is allowed
+ *   gamma, beta     [tokens/tokens_per_row][d_model] float32
+ *   tokens > 0, tokens % tokens_per_row == 0, eps > 0
+ *   d_model % 8 == 0 and 8 <= d_model <= 8192 (else DIT_E_UNSUPPORTED)
+ */
+int dit_adaln_modulate(void* y, const void* x, const float* gamma, const float* beta,
+                       int64_t tokens, int32_t d_model, int64_t tokens_per_row,
+                       float eps, int32_t dtype, void* stream);
+
+/*
+ * 3D rotary position embedding in place on q and k, "DiT, Flow Matching e 3D
+ * Attention", section "3D-RoPE e atencao espaco-temporal": d_head = d_t + d_h + d_w
+ * and q_rot = R_3D(t, y, x) q, k_rot = R_3D(t, y, x) k. Slices are laid out
+ * [t | h | w]; pair j of the slice for axis a (width d_a, offset o_a) covers dims
+ * (o_a + 2j, o_a + 2j + 1) and turns by phi = pos_a * base^(-2j / d_a):
+ *   (x0, x1) <- (x0 cos phi - x1 sin phi, x0 sin phi + x1 cos phi).
+ * Every head of a token uses the same rotation. v is not rotated.
+ *
+ *   q, k         [tokens][heads][head_dim] (dtype), rotated in place; k may be NULL
+ *   grid_h, grid_w   patched H', W' of every sequence
+ *   dense mode  (cu_seqlens == NULL): num_seqs sequences of grid_t*grid_h*grid_w
+ *                tokens each; tokens must equal num_seqs * grid_t * grid_h * grid_w
+ *   packed mode (cu_seqlens != NULL): device int32 [num_seqs+1]; grid_t is
+ *                ignored; each sequence length must be a multiple of grid_h*grid_w
+ *                (unchecked precondition). Positions restart at 0 per sequence.
+ *   d_t, d_h, d_w    even, >= 0, summing to head_dim; base > 1
+ *   pos_out      nullable device int32 [tokens][3]: receives (t', h', w')
+ *   head_dim % 8 == 0 and head_dim <= 256, heads >= 1
+ */
+int dit_rope3d(void* q, void* k, int64_t tokens, int32_t heads, int32_t head_dim,
+               int32_t grid_t, int32_t grid_h, int32_t grid_w,
+               const int32_t* cu_seqlens, int32_t num_seqs,
+               int32_t d_t, int32_t d_h, int32_t d_w, float base,
+               int32_t* pos_out, int32_t dtype, void* stream);
+
+/*
+ * Full spatio-temporal attention, "Por que e absurdamente dificil gerar um filme
+ * inteiro usando IA", section "Matematica por tras", with the scale of "DiT, Flow
+ * Matching e 3D Attention", section "3D-RoPE e atencao espaco-temporal":
+ *   o[i][h] = sum_j softmax_j(q[i][h] . k[j][h] / sqrt(head_dim)) v[j][h]
+ * over every key j of the query's own sequence (bidirectional, no mask; packed
+ * sequences never attend to each other).
+ *
+ *   o, q, k, v   [tokens][heads][head_dim] (dtype); o must not overlap q, k or v
+ *   dense mode  (cu_seqlens == NULL): num_seqs sequences of tokens/num_seqs tokens
+ *   packed mode (cu_seqlens != NULL): device int32 [num_seqs+1]; max_seqlen must
+ *                be >= every sequence length (unchecked precondition)
+ *   head_dim in {64, 128} (else DIT_E_UNSUPPORTED)
+ * bf16 runs on MFMA with float32 accumulation; probabilities enter the second
+ * product rounded to bf16. float32 runs on the vector ALUs in full float32.
+ */
+int dit_attn3d(void* o, const void* q, const void* k, const void* v,
+               int64_t tokens, int32_t heads, int32_t head_dim,
+               const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+               int32_t dtype, void* stream);
+
+/* Optional Euler pass fused into dit_gated_residual (same launch, same dtype). */
+typedef struct {
+    void* z_out;            /* [tokens][channels]; may equal z */
+    const void* z;          /* [tokens][channels] */
+    const void* u;          /* [tokens][channels] velocity */
+    const float* dt_rows;   /* [tokens/tokens_per_row] float32 */
+    int64_t tokens;
+    int32_t channels;
+    int64_t tokens_per_row;
+} dit_euler_args;
+
+/*
+ * Gated residual, "DiT, Flow Matching e 3D Attention", section "A ruptura da
+ * U-Net" (x'_l = x_l + alpha_1 * SelfAttention(...); alpha = 0 gives the identity):
+ *   x_out[tok][c] = x[tok][c] + alpha[row][c] * branch[tok][c],  row = tok / tokens_per_row
+ * branch is the attention output with heads merged (c = h * head_dim + i).
+ *
+ *   x_out, x, branch   [tokens][d_model] (dtype); x_out == x allowed
+ *   alpha              [tokens/tokens_per_row][d_model] float32
+ *   euler              nullable: also run rf_euler_step's update in the same launch
+ *   d_model % 8 == 0
+ */
+int dit_gated_residual(void* x_out, const void* x, const void* branch, const float* alpha,
+                       int64_t tokens, int32_t d_model, int64_t tokens_per_row,
+                       const dit_euler_args* euler, int32_t dtype, void* stream);
+
+/*
+ * Rectified-flow Euler step, "DiT, Flow Matching e 3D Attention", section "Flow
+ * Matching e Rectified Flow": along x_t = (1-t) x_0 + t x_1 (noise at t = 0, data at
+ * t = 1) the velocity is x_1 - x_0 and an Euler sampler advances
+ *   z_out[tok][c] = z[tok][c] + dt_rows[row] * u[tok][c],   row = tok / tokens_per_row
+ * (one dt per sample, or per frame for per-frame local times).
+ *
+ *   z_out, z, u   [tokens][channels] (dtype); z_out == z allowed
+ *   dt_rows       [tokens/tokens_per_row] float32
+ *   channels % 8 == 0
+ */
+int rf_euler_step(void* z_out, const void* z, const void* u, const float* dt_rows,
+                  int64_t tokens, int32_t channels, int64_t tokens_per_row,
+                  int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_H_ */

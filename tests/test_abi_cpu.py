@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every symbol include/dit.h declares, and
+rejects bad arguments before touching the device (CPU only: every call below
+fails validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import diffusion_transformer_video_amd as dit
+from libdit_loader import ensure_built
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dit.h")
+FAKE = 0x10000  # aligned, never dereferenced: every call here fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("dit_adaln_modulate", "dit_rope3d", "dit_attn3d", "dit_gated_residual",
+              "rf_euler_step", "dit_last_error", "dit_version"):
+        assert n in names
+    assert set(names) == set(dit.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ensure_built()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert L.dit_version() == 10000
+
+
+def _err():
+    return dit.lib().dit_last_error().decode()
+
+
+def test_modulate_validation():
+    L = ensure_built()
+    assert L.dit_adaln_modulate(None, FAKE, FAKE, FAKE, 8, 64, 8, 1e-6, 1, None) == dit.DIT_E_INVAL
+    assert "NULL" in _err()
+    assert L.dit_adaln_modulate(FAKE, FAKE, FAKE, FAKE, 0, 64, 1, 1e-6, 1, None) == dit.DIT_E_INVAL
+    assert L.dit_adaln_modulate(FAKE, FAKE, FAKE, FAKE, 10, 64, 3, 1e-6, 1, None) == dit.DIT_E_INVAL
+    assert "tokens_per_row" in _err()
+    assert L.dit_adaln_modulate(FAKE, FAKE, FAKE, FAKE, 8, 64, 8, 0.0, 1, None) == dit.DIT_E_INVAL
+    assert L.dit_adaln_modulate(FAKE, FAKE, FAKE, FAKE, 8, 60, 8, 1e-6, 1, None) == dit.DIT_E_UNSUPPORTED
+    assert L.dit_adaln_modulate(FAKE, FAKE, FAKE, FAKE, 8, 64, 8, 1e-6, 7, None) == dit.DIT_E_UNSUPPORTED
+    assert "dtype" in _err()
+    assert L.dit_adaln_modulate(FAKE + 4, FAKE, FAKE, FAKE, 8, 64, 8, 1e-6, 1, None) == dit.DIT_E_UNSUPPORTED
+    assert "aligned" in _err()
+    # y partially overlapping x
+    assert L.dit_adaln_modulate(FAKE + 16, FAKE, FAKE * 4, FAKE * 8, 8, 64, 8, 1e-6, 1, None) == dit.DIT_E_INVAL
+
+
+def test_rope_validation():
+    L = ensure_built()
+    args = dict(q=FAKE, k=FAKE * 8, tokens=32, heads=2, hd=64, gt=2, gh=4, gw=4, cu=None, ns=1,
+                dt_=16, dh=24, dw=24, base=10000.0, pos=None, dtype=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.dit_rope3d(a["q"], a["k"], a["tokens"], a["heads"], a["hd"], a["gt"], a["gh"], a["gw"],
+                            a["cu"], a["ns"], a["dt_"], a["dh"], a["dw"], a["base"], a["pos"], a["dtype"], None)
+    assert call(q=None) == dit.DIT_E_INVAL
+    assert call(dh=26) == dit.DIT_E_INVAL and "head_dim" in _err()
+    assert call(dt_=15, dh=25) == dit.DIT_E_INVAL and "even" in _err()
+    assert call(base=1.0) == dit.DIT_E_INVAL
+    assert call(tokens=33) == dit.DIT_E_INVAL and "dense" in _err()
+    assert call(gt=0) == dit.DIT_E_INVAL
+    assert call(hd=96, dt_=32, dh=32, dw=32, tokens=32) == dit.DIT_E_UNSUPPORTED
+    assert call(k=FAKE + 64) == dit.DIT_E_INVAL and "overlap" in _err()
+
+
+def test_attn_validation():
+    L = ensure_built()
+    o, q, k, v = FAKE * 16, FAKE, FAKE * 4, FAKE * 8
+    assert L.dit_attn3d(None, q, k, v, 64, 2, 128, None, 1, 0, 1, None) == dit.DIT_E_INVAL
+    assert L.dit_attn3d(o, q, k, v, 65, 2, 128, None, 2, 0, 1, None) == dit.DIT_E_INVAL
+    assert "multiple of num_seqs" in _err()
+    assert L.dit_attn3d(o, q, k, v, 64, 2, 96, None, 1, 0, 1, None) == dit.DIT_E_UNSUPPORTED
+    assert L.dit_attn3d(o, q, k, v, 64, 2, 128, FAKE * 32, 2, 0, 1, None) == dit.DIT_E_INVAL
+    assert "max_seqlen" in _err()
+    assert L.dit_attn3d(q, q, k, v, 64, 2, 128, None, 1, 0, 1, None) == dit.DIT_E_INVAL
+    assert "overlap" in _err()
+    assert L.dit_attn3d(o, q, k, v, 0, 2, 128, None, 1, 0, 1, None) == dit.DIT_E_INVAL
+
+
+def test_epilogue_validation():
+    L = ensure_built()
+    assert L.rf_euler_step(FAKE, FAKE, FAKE * 4, None, 32, 64, 32, 1, None) == dit.DIT_E_INVAL
+    assert L.rf_euler_step(FAKE, FAKE, FAKE * 4, FAKE * 8, 32, 60, 32, 1, None) == dit.DIT_E_UNSUPPORTED
+    assert L.rf_euler_step(FAKE, FAKE, FAKE, FAKE * 8, 32, 64, 32, 1, None) == dit.DIT_E_INVAL
+    assert "overlaps u" in _err()
+    assert L.dit_gated_residual(FAKE, FAKE, FAKE * 4, FAKE * 8, 30, 64, 7, None, 1, None) == dit.DIT_E_INVAL
+    bad = dit.EulerArgs(FAKE * 16, FAKE * 16, FAKE * 20, None, 32, 64, 32)
+    assert L.dit_gated_residual(FAKE, FAKE, FAKE * 4, FAKE * 8, 32, 64, 32, ctypes.byref(bad), 1,
+                                None) == dit.DIT_E_INVAL
+    assert "euler" in _err()
+
+
+def test_error_text_is_thread_local_and_cleared_on_new_error():
+    L = ensure_built()
+    L.rf_euler_step(None, None, None, None, 0, 0, 0, 1, None)
+    first = _err()
+    L.dit_attn3d(None, None, None, None, 1, 1, 64, None, 1, 0, 1, None)
+    assert _err() != first and _err().startswith("dit_attn3d")
+
+
+def test_binding_raises_without_gpu_tensors():
+    import torch
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        dit.rf_euler_step(x, x, x, torch.zeros(1), 4)
