@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle sample")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="after timing, run a plain device copy of this many MiB (read once, "
+                        "written once) so hardware byte counters can be scaled against it")
     return p.parse_args()
 
 
@@ -178,6 +181,15 @@ def main():
                      "flops_per_launch": flops},
         "kernels": kernels,
     }
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)   # elementwise: reads n*4 bytes, writes n*4 bytes
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = n * 4
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

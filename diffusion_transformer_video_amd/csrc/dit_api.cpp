@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -191,6 +192,10 @@ int dit_attn3d(void* o, const void* q, const void* k, const void* v,
         return fail(DIT_E_UNSUPPORTED, "%s: head_dim must be 64 or 128 (got %d)", fn, head_dim);
     if (!aligned16(o) || !aligned16(q) || !aligned16(k) || !aligned16(v))
         return fail(DIT_E_UNSUPPORTED, "%s: tensors must be 16-byte aligned", fn);
+    // the bf16 kernel addresses one sequence of one head with 32-bit byte offsets
+    if ((int64_t)seqlen * heads * head_dim * elem_size(dtype) > INT32_MAX)
+        return fail(DIT_E_UNSUPPORTED, "%s: sequence length x heads x head_dim too large (%lld bytes per sequence)",
+                    fn, (long long)seqlen * heads * head_dim * elem_size(dtype));
     const int64_t bytes = tokens * heads * head_dim * elem_size(dtype);
     if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
         return fail(DIT_E_INVAL, "%s: o must not overlap q, k or v", fn);

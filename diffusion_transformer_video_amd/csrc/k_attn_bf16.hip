@@ -50,111 +50,196 @@ struct Cfg {
     static constexpr int NT = 64 * NW;         // threads per block
     static constexpr int BQ = 32 * NW;         // queries per block
     static constexpr int BK = 64;              // keys per tile
-    static constexpr int KSTR = HD * 2 + 16;   // bytes per K row in LDS
-    static constexpr int VSTR = BK * 2 + 16;   // bytes per V^T row in LDS
-    static constexpr int KBYTES = BK * KSTR;
-    static constexpr int VBYTES = HD * VSTR;
-    static constexpr int BUF = KBYTES + VBYTES;
-    static constexpr int LDS = 2 * BUF;
+    static constexpr int ROWB = HD * 2;        // bytes per K / V row in LDS (no padding)
+    static constexpr int CPR = HD / 8;         // 16-byte chunks per row
+    static constexpr int RPB = 1024 / ROWB;    // rows per 1 KB block (one wave-wide load)
+    static constexpr int KBYTES = BK * ROWB;
+    static constexpr int BUF = 2 * KBYTES;     // K tile + V tile
+    // double buffered: two separate LDS objects, so the compiler can tell that
+    // the loads streaming into one never alias the reads of the other
+    static constexpr int NBLK = KBYTES / 1024; // 1 KB blocks per K (or V) tile
+    static constexpr int LPW = NBLK / NW;      // K (and V) block loads per wave per tile
     static constexpr int NKK = HD / 16;        // k-steps of the S^T product
     static constexpr int NDT = HD / 32;        // 32-wide d tiles of O^T
-    static constexpr int CPR = HD / 8;         // 16-byte chunks per row
-    static constexpr int KCH = BK * CPR / NT;  // K chunks per thread per tile
-    static constexpr int VK = (BK / 4) * CPR >= NT ? 4 : 2;   // keys per V unit
-    static constexpr int VUN = (BK / VK) * CPR / NT;           // V units per thread
-    static_assert(KCH >= 1 && KCH * NT == BK * CPR, "K staging must tile evenly");
-    static_assert(VUN >= 1 && VUN * NT == (BK / VK) * CPR, "V staging must tile evenly");
-    // staging registers of one tile (ext vectors stay in VGPRs; C arrays may not)
-    typedef uint32_t KStage __attribute__((ext_vector_type(4 * KCH)));
-    typedef uint32_t VStage __attribute__((ext_vector_type(4 * VUN * VK)));
+    static_assert(LPW >= 1 && LPW * NW == NBLK, "tile loads must split evenly over the waves");
+    static_assert(CPR == 8 || CPR == 16, "head_dim 64 or 128");
 };
 
-// Position of key `k` (0..BK-1) inside a V^T row: within each group of 16 keys,
-// bits 2 and 3 of the offset are swapped, so that the 8 contraction slots of
-// lane group g for MFMA step t are the 8 consecutive positions 16t + 8g .. +7.
-__device__ __forceinline__ int vt_pos(int k) {
-    const int o = k & 15;
-    return (k & ~15) | (((o >> 2) & 1) << 3) | (((o >> 3) & 1) << 2) | (o & 3);
+// LDS swizzles (16-byte chunk granularity; rows are unpadded so whole 1 KB
+// blocks arrive by direct global->LDS loads in lane order).
+//  K: chunk c of row r sits at c ^ kswz(r). The K operand read of 16 lanes takes
+//     16 consecutive rows at one logical chunk; the XOR spreads them over all
+//     64 banks.
+//  V: chunk c of key row r sits at c ^ vswz(r). A transposed read takes 4
+//     consecutive key rows x 32 bytes per 16 lanes (64 bytes per 32 lanes); the
+//     XOR moves the 4 rows onto disjoint chunk groups.
+template <int CPR>
+__device__ __forceinline__ int kswz(int r) { return (r / (16 / CPR)) & (CPR - 1); }
+template <int CPR>
+__device__ __forceinline__ int vswz(int r) { return 4 * ((r / (16 / CPR)) % (CPR / 4)); }
+
+// Max / sum of x over the lane pair (l, l ^ 32): v_permlane32_swap exchanges the
+// upper half of the first operand with the lower half of the second, so with
+// both operands = x the two results hold (own, partner) in some order per lane.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Issue the direct global->LDS loads of one K/V tile (keys kbase..kbase+63 of
+// the sequence) into LDS buffer `dst`. Wave w moves 1 KB blocks w, w+NW, ... of
+// K and of V; in a block, lane L carries row RPB*blk + L/CPR, physical chunk
+// L%CPR (hence logical chunk (L%CPR) ^ swizzle(row)). FULL: every row is inside
+// the sequence and the per-lane offset is loop-invariant (rows step by the
+// scalar offset); otherwise rows past the end are clamped to the last row.
+template <int HD, int NW, bool FULL>
+__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                           char* dst, int wave, int lane, uint32_t ldb,
+                                           uint32_t kbase, uint32_t rows_left,
+                                           uint32_t koff, uint32_t voff) {
+    using C = Cfg<HD, NW>;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+        const int blk = wave + NW * i;
+        const uint32_t row_step = (uint32_t)(C::RPB * NW * i);   // rows added by block i
+        uint32_t ko = koff, vo = voff, so = (kbase + row_step) * ldb;
+        if (!FULL) {
+            const uint32_t r0 = (uint32_t)(C::RPB * wave + lane / C::CPR) + row_step;
+            const uint32_t r = r0 < rows_left ? r0 : rows_left - 1;
+            const uint32_t pc = (uint32_t)(lane % C::CPR);
+            ko = r * ldb + ((pc ^ (uint32_t)kswz<C::CPR>((int)r0)) * 16);
+            vo = r * ldb + ((pc ^ (uint32_t)vswz<C::CPR>((int)r0)) * 16);
+            so = kbase * ldb;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(dst + blk * 1024), 16, (int)ko, (int)so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(dst + C::KBYTES + blk * 1024), 16, (int)vo,
+                                                 (int)so, 0, 0);
+    }
 }
 
 template <int HD, int NW>
-__device__ __forceinline__ void load_tile(const uint4* __restrict__ Kg, const uint4* __restrict__ Vg,
-                                          int64_t ld16, int64_t len, int tid, int j,
-                                          typename Cfg<HD, NW>::KStage& kst,
-                                          typename Cfg<HD, NW>::VStage& vst) {
+__device__ __forceinline__ void issue_tile_any(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                               char* dst, int wave, int lane, uint32_t ldb,
+                                               uint32_t kbase, uint32_t len, uint32_t koff, uint32_t voff) {
+    if (kbase + Cfg<HD, NW>::BK <= len)
+        issue_tile<HD, NW, true>(rk, rv, dst, wave, lane, ldb, kbase, len - kbase, koff, voff);
+    else
+        issue_tile<HD, NW, false>(rk, rv, dst, wave, lane, ldb, kbase, len - kbase, koff, voff);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// V^T operand for one MFMA step: 4 consecutive keys at Vaddr and 4 more 8 keys
+// later (the two halves of the lane's 8 contraction slots), transposed on read.
+__device__ __forceinline__ bf16x8 vt_operand(const char* Vaddr, int second) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(Vaddr));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(Vaddr + second));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Online-softmax update for one 32-key block of S^T (this lane: one query, 16
+// keys) followed by its two MFMA steps of O^T += V^T P^T. The running max is only
+// raised when the block max exceeds it by more than 2^kLazyRescale (wave-uniform
+// branch, rare after the first block). Probabilities are rounded to bf16 for the
+// MFMA, and the row sum accumulates exactly those rounded values (v_dot2 with
+// ones), so the normalisation uses the weights the product used.
+//
+// vt[dt] points at this lane's V^T source for d tile dt, key block 0, step 0 of
+// the current buffer; key block kb / step t / second half add
+// (32kb + 16t + 8h) rows.
+template <int HD, int NW, bool MASK>
+__device__ __forceinline__ void block_softmax_pv(f32x16& S, const char* const (&vt)[Cfg<HD, NW>::NDT],
+                                                 int kb, f32x16 (&O)[Cfg<HD, NW>::NDT], float& m_run,
+                                                 float& l_run, float c, int g, int kofs0, int len) {
     using C = Cfg<HD, NW>;
-    const int64_t kbase = (int64_t)j * C::BK;
+    if constexpr (MASK) {
 #pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-        const int u = tid + C::NT * i;
-        const int row = u / C::CPR, c = u % C::CPR;
-        int64_t kr = kbase + row;
-        kr = kr < len ? kr : len - 1;
-        const uint4 t = Kg[kr * ld16 + c];
-        kst[4 * i + 0] = t.x; kst[4 * i + 1] = t.y; kst[4 * i + 2] = t.z; kst[4 * i + 3] = t.w;
+        for (int r = 0; r < 16; ++r)
+            if (kofs0 + 8 * (r >> 2) + 4 * g + (r & 3) >= len) S[r] = -INFINITY;
     }
+    float mx = __builtin_fmaxf(S[0], __builtin_fmaxf(S[1], S[2]));
 #pragma unroll
-    for (int i = 0; i < C::VUN; ++i) {
-        const int u = tid + C::NT * i;
-        const int c = u % C::CPR, kgp = u / C::CPR;
+    for (int r = 3; r < 15; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(S[r], S[r + 1]));
+    mx = __builtin_fmaxf(mx, S[15]);
+    const float mxs = pair_max(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0) {
+        const float m_new = __builtin_fmaxf(m_run, mxs);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-        for (int r = 0; r < C::VK; ++r) {
-            int64_t kr = kbase + kgp * C::VK + r;
-            kr = kr < len ? kr : len - 1;
-            const uint4 t = Vg[kr * ld16 + c];
-            const int o = 4 * (i * C::VK + r);
-            vst[o + 0] = t.x; vst[o + 1] = t.y; vst[o + 2] = t.z; vst[o + 3] = t.w;
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+        m_run = m_new;
+    }
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(S[8 * t + 2 * e], c, -m_run));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(S[8 * t + 2 * e + 1], c, -m_run));
+            w[e] = pack_bf16x2(p0, p1);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), ones, l_run, false);
+        }
+        const bf16x8 P = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) {
+            const bf16x8 v = vt_operand(vt[dt] + (32 * kb + 16 * t) * C::ROWB, 8 * C::ROWB);
+            O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, P, O[dt], 0, 0, 0);
         }
     }
 }
 
-template <int HD, int NW>
-__device__ __forceinline__ void store_tile(char* smem, int tid, int buf,
-                                           const typename Cfg<HD, NW>::KStage& kst,
-                                           const typename Cfg<HD, NW>::VStage& vst) {
+// One key tile of 64 keys in LDS buffer `buf`: S^T = K Q^T (two 32-key blocks)
+// on MFMA, then per block the online softmax and O^T += V^T P^T on MFMA, so the
+// second block's softmax can overlap the first block's products.
+// kaddr[kk]: this lane's K operand address for k-step kk (row l32 of key block 0)
+// in buffer 0; MASK: the tile may extend past the sequence end.
+template <int HD, int NW, bool MASK>
+__device__ __forceinline__ void tile_step(const char* bufp, const int (&kaddr)[Cfg<HD, NW>::NKK],
+                                          const int (&vaddr)[Cfg<HD, NW>::NDT],
+                                          const bf16x8 (&qreg)[Cfg<HD, NW>::NKK],
+                                          f32x16 (&O)[Cfg<HD, NW>::NDT], float& m_run, float& l_run,
+                                          float c, int g, int kbase, int len) {
     using C = Cfg<HD, NW>;
-    char* Kb = smem + buf * C::BUF;
-    char* Vb = Kb + C::KBYTES;
+    f32x16 S0, S1;
 #pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-        const int u = tid + C::NT * i;
-        const int row = u / C::CPR, c = u % C::CPR;
-        *reinterpret_cast<uint4*>(Kb + row * C::KSTR + c * 16) =
-            make_uint4(kst[4 * i + 0], kst[4 * i + 1], kst[4 * i + 2], kst[4 * i + 3]);
+    for (int r = 0; r < 16; ++r) { S0[r] = 0.f; S1[r] = 0.f; }
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(bufp + kaddr[kk]);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(bufp + kaddr[kk] + 32 * C::ROWB);
+        S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], S0, 0, 0, 0);
+        S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], S1, 0, 0, 0);
     }
+    const char* vt[C::NDT];
 #pragma unroll
-    for (int i = 0; i < C::VUN; ++i) {
-        const int u = tid + C::NT * i;
-        const int c = u % C::CPR, kgp = u / C::CPR;
-        const int pos = vt_pos(kgp * C::VK);
-        // word p of the 16-byte row r of this unit: dims c*8 + 2p, c*8 + 2p + 1
-#define VW(r, p) vst[4 * (i * C::VK + (r)) + (p)]
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int d = c * 8 + 2 * p;
-            char* dst_e = Vb + d * C::VSTR + pos * 2;
-            char* dst_o = dst_e + C::VSTR;
-            if constexpr (C::VK == 4) {
-                uint2 ev, od;
-                ev.x = (VW(0, p) & 0xffffu) | (VW(1, p) << 16);
-                ev.y = (VW(2, p) & 0xffffu) | (VW(3, p) << 16);
-                od.x = (VW(0, p) >> 16) | (VW(1, p) & 0xffff0000u);
-                od.y = (VW(2, p) >> 16) | (VW(3, p) & 0xffff0000u);
-                *reinterpret_cast<uint2*>(dst_e) = ev;
-                *reinterpret_cast<uint2*>(dst_o) = od;
-            } else {
-                *reinterpret_cast<uint32_t*>(dst_e) = (VW(0, p) & 0xffffu) | (VW(1, p) << 16);
-                *reinterpret_cast<uint32_t*>(dst_o) = (VW(0, p) >> 16) | (VW(1, p) & 0xffff0000u);
-            }
-        }
-#undef VW
-    }
+    for (int dt = 0; dt < C::NDT; ++dt) vt[dt] = bufp + vaddr[dt];
+    block_softmax_pv<HD, NW, MASK>(S0, vt, 0, O, m_run, l_run, c, g, kbase, len);
+    block_softmax_pv<HD, NW, MASK>(S1, vt, 1, O, m_run, l_run, c, g, kbase + 32, len);
 }
 
 template <int HD, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a, int nqt) {
     using C = Cfg<HD, NW>;
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    __shared__ __attribute__((aligned(1024))) char smem0[C::BUF];
+    __shared__ __attribute__((aligned(1024))) char smem1[C::BUF];
 
     // ---- block -> (sequence, head, query tile), XCD-contiguous numbering
     const int total = (int)gridDim.x;
@@ -162,36 +247,73 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a, int n
     const int per = total / 8, rem = total % 8;
     const int xcd = b % 8, idx = b / 8;
     const int w = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-    const int qt = w % nqt;
-    const int head = (w / nqt) % a.heads;
-    const int seq = w / (nqt * a.heads);
+    // the divisions run on the vector ALU; the results are block-uniform
+    const int qt = __builtin_amdgcn_readfirstlane(w % nqt);
+    const int head = __builtin_amdgcn_readfirstlane((w / nqt) % a.heads);
+    const int seq = __builtin_amdgcn_readfirstlane(w / (nqt * a.heads));
 
-    int64_t s0, len;
+    int64_t s0;
+    int len;
     if (a.cu_seqlens == nullptr) {
         s0 = (int64_t)seq * a.max_seqlen;
         len = a.max_seqlen;
     } else {
-        s0 = a.cu_seqlens[seq];
-        len = (int64_t)a.cu_seqlens[seq + 1] - s0;
+        // uniform per block: keep them in SGPRs so the buffer descriptors are scalar
+        const int c0 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq]);
+        const int c1 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq + 1]);
+        s0 = c0;
+        len = c1 - c0;
     }
-    const int64_t q0 = (int64_t)qt * C::BQ;
+    const int q0 = qt * C::BQ;
     if (q0 >= len) return;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
-    const int64_t ld16 = (int64_t)a.heads * C::CPR;   // token stride in 16-byte chunks
-    const uint4* Qg = reinterpret_cast<const uint4*>(a.q) + s0 * ld16 + (int64_t)head * C::CPR;
-    const uint4* Kg = reinterpret_cast<const uint4*>(a.k) + s0 * ld16 + (int64_t)head * C::CPR;
-    const uint4* Vg = reinterpret_cast<const uint4*>(a.v) + s0 * ld16 + (int64_t)head * C::CPR;
+    const uint32_t ldb = (uint32_t)a.heads * HD * 2;   // token stride in bytes
+    const int64_t base = (s0 * a.heads + head) * (int64_t)HD;   // element offset of (s0, head, 0)
+    const uint32_t span = (uint32_t)len * ldb;        // bytes of this sequence (< 2^31, host-checked)
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const __bf16*>(a.q) + base), (short)0, span, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const __bf16*>(a.k) + base), (short)0, span, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const __bf16*>(a.v) + base), (short)0, span, 0x00020000);
+
+    // ---- per-lane, loop-invariant offsets
+    // direct loads: lane carries row RPB*wave + lane/CPR of each of its blocks
+    const int lrow = C::RPB * wave + lane / C::CPR;
+    const int pc = lane % C::CPR;
+    const uint32_t koff = (uint32_t)lrow * ldb + (uint32_t)((pc ^ kswz<C::CPR>(lrow)) * 16);
+    const uint32_t voff = (uint32_t)lrow * ldb + (uint32_t)((pc ^ vswz<C::CPR>(lrow)) * 16);
+    // K operand (A of S^T): row l32, logical chunk 2kk + g
+    int kaddr[C::NKK];
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk)
+        kaddr[kk] = l32 * C::ROWB + (((2 * kk + g) ^ kswz<C::CPR>(l32)) * 16);
+    // V^T operand (A of O^T): 16-lane group hg = lane/16 covers d = 32dt + 16(hg%2) + i
+    // (i = lane%16); its source lanes point at key row 4g + i/4 (+ block offsets),
+    // 4 dims starting at 32dt + 16(hg%2) + 4(i%4).
+    int vaddr[C::NDT];
+    {
+        const int i16 = lane & 15, hg = lane >> 4;
+        const int vrow = 4 * g + i16 / 4;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) {
+            const int d0 = 32 * dt + 16 * (hg & 1) + 4 * (i16 & 3);   // first dim of the 8-byte piece
+            const int chunk = (d0 / 8) ^ vswz<C::CPR>(vrow);
+            vaddr[dt] = C::KBYTES + vrow * C::ROWB + chunk * 16 + (d0 % 8) * 2;
+        }
+    }
 
     // ---- Q (B operand of S^T = K Q^T): lane holds query l32, d = 16kk + 8g .. +7
-    const int64_t my_q = q0 + wave * 32 + l32;
-    const int64_t qrow = my_q < len ? my_q : len - 1;
+    const int my_q = q0 + wave * 32 + l32;
+    const uint32_t qrow = (uint32_t)(my_q < len ? my_q : len - 1);
     bf16x8 qreg[C::NKK];
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk)
-        qreg[kk] = __builtin_bit_cast(bf16x8, Qg[qrow * ld16 + 2 * kk + g]);
+        qreg[kk] = __builtin_bit_cast(bf16x8, bload(rq, qrow * ldb + (2 * kk + g) * 16, 0));
 
     f32x16 O[C::NDT];
 #pragma unroll
@@ -200,104 +322,42 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a, int n
         for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
     float m_run = -INFINITY;   // running max in the scaled log2 domain
     float l_run = 0.f;         // this lane's partial row sum (its 16 keys per tile)
-
-    typename C::KStage kst;
-    typename C::VStage vst;
-    const int ntiles = (int)((len + C::BK - 1) / C::BK);
-
-    load_tile<HD, NW>(Kg, Vg, ld16, len, tid, 0, kst, vst);
-    store_tile<HD, NW>(smem, tid, 0, kst, vst);
-    __syncthreads();
-
     const float c = a.scale_log2;
-    for (int j = 0; j < ntiles; ++j) {
-        const int buf = j & 1;
-        const bool more = (j + 1) < ntiles;
-        if (more) load_tile<HD, NW>(Kg, Vg, ld16, len, tid, j + 1, kst, vst);
+    const int ntiles = (len + C::BK - 1) / C::BK;
 
-        const char* Kb = smem + buf * C::BUF;
-        const char* Vb = Kb + C::KBYTES;
-
-        // ---- S^T = K Q^T for 2 blocks of 32 keys
-        f32x16 S0, S1;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { S0[r] = 0.f; S1[r] = 0.f; }
-#pragma unroll
-        for (int kk = 0; kk < C::NKK; ++kk) {
-            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(Kb + l32 * C::KSTR + kk * 32 + g * 16);
-            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(Kb + (32 + l32) * C::KSTR + kk * 32 + g * 16);
-            S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], S0, 0, 0, 0);
-            S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], S1, 0, 0, 0);
+    issue_tile_any<HD, NW>(rk, rv, smem0, wave, lane, ldb, 0, (uint32_t)len, koff, voff);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // tile j+1 streams into one buffer while tile j is consumed from the other;
+    // unrolled by two so each buffer is a distinct object at every access
+    for (int j = 0;;) {
+        if (j + 1 >= ntiles) {
+            tile_step<HD, NW, true>(smem0, kaddr, vaddr, qreg, O, m_run, l_run, c, g, j * C::BK, len);
+            break;
         }
-
-        // ---- mask keys past the sequence end (last tile only)
-        if (!more) {
-            const int64_t kbase = (int64_t)j * C::BK;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kofs = 8 * (r >> 2) + 4 * g + (r & 3);
-                if (kbase + kofs >= len) S0[r] = -INFINITY;
-                if (kbase + 32 + kofs >= len) S1[r] = -INFINITY;
-            }
-        }
-
-        // ---- online softmax (exp2 domain, lazy max)
-        float mx = fmaxf(S0[0], S1[0]);
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mxs = mx * c;
-        if (__builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0) {
-            const float m_new = fmaxf(m_run, mxs);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
-            m_run = m_new;
-        }
-        // probabilities -> bf16 B operands: key block kb, MFMA step t (8 keys each)
-        auto exp_pack = [&](const f32x16& S, int t) -> bf16x8 {
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = __builtin_amdgcn_exp2f(fmaf(S[8 * t + e], c, -m_run));
-                l_run += p[e];
-            }
-            uint4 wv;
-            wv.x = pack_bf16x2(p[0], p[1]); wv.y = pack_bf16x2(p[2], p[3]);
-            wv.z = pack_bf16x2(p[4], p[5]); wv.w = pack_bf16x2(p[6], p[7]);
-            return __builtin_bit_cast(bf16x8, wv);
-        };
-        const bf16x8 P00 = exp_pack(S0, 0), P01 = exp_pack(S0, 1);
-        const bf16x8 P10 = exp_pack(S1, 0), P11 = exp_pack(S1, 1);
-
-        // ---- O^T += V^T P^T
-        const char* Vrow = Vb + l32 * C::VSTR + 16 * g;
-#pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) {
-            const char* vr = Vrow + dt * 32 * C::VSTR;
-            const bf16x8 v00 = *reinterpret_cast<const bf16x8*>(vr + 0);
-            const bf16x8 v01 = *reinterpret_cast<const bf16x8*>(vr + 32);
-            const bf16x8 v10 = *reinterpret_cast<const bf16x8*>(vr + 64);
-            const bf16x8 v11 = *reinterpret_cast<const bf16x8*>(vr + 96);
-            O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v00, P00, O[dt], 0, 0, 0);
-            O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v01, P01, O[dt], 0, 0, 0);
-            O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v10, P10, O[dt], 0, 0, 0);
-            O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v11, P11, O[dt], 0, 0, 0);
-        }
-
-        if (more) store_tile<HD, NW>(smem, tid, buf ^ 1, kst, vst);
+        issue_tile_any<HD, NW>(rk, rv, smem1, wave, lane, ldb, (uint32_t)(j + 1) * C::BK, (uint32_t)len,
+                               koff, voff);
+        tile_step<HD, NW, false>(smem0, kaddr, vaddr, qreg, O, m_run, l_run, c, g, j * C::BK, len);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        ++j;
+        if (j + 1 >= ntiles) {
+            tile_step<HD, NW, true>(smem1, kaddr, vaddr, qreg, O, m_run, l_run, c, g, j * C::BK, len);
+            break;
+        }
+        issue_tile_any<HD, NW>(rk, rv, smem0, wave, lane, ldb, (uint32_t)(j + 1) * C::BK, (uint32_t)len,
+                               koff, voff);
+        tile_step<HD, NW, false>(smem1, kaddr, vaddr, qreg, O, m_run, l_run, c, g, j * C::BK, len);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        ++j;
     }
 
     // ---- normalise and store: lane holds query l32, d = 32dt + 8(r/4) + 4g + r%4
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    const float inv = 1.0f / l_tot;
+    const float inv = 1.0f / pair_sum(l_run);   // lanes l and l^32 summed disjoint keys
     if (my_q < len) {
-        uint2* Og = reinterpret_cast<uint2*>(reinterpret_cast<uint4*>(a.o) + (s0 + my_q) * ld16 +
-                                             (int64_t)head * C::CPR);
+        uint2* Og = reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(a.o) + base +
+                                             (int64_t)my_q * a.heads * HD);
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) {
 #pragma unroll
