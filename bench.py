@@ -97,50 +97,96 @@ def main():
     grid = (w.frames[0], *w.grid_hw)
     del inp
 
-    names = ("modulate", "rope", "attn", "residual_euler")
-    ev = {n: [] for n in names}
+    def launch(name):
+        if name == "modulate":
+            dit.dit_adaln_modulate(y, x, g, b, w.tokens_per_row, w.eps)
+        elif name == "rope":
+            dit.dit_rope3d(q, k, grid, w.rope_split, w.rope_base, cu_seqlens=cu, num_seqs=w.num_seqs)
+        elif name == "attn":
+            if cu is None:
+                dit.dit_attn3d(o, q, k, v, num_seqs=w.num_seqs)
+            else:
+                dit.dit_attn3d(o, q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen)
+        else:
+            dit.dit_gated_residual(x_out, x, o2d, al, w.tokens_per_row,
+                                   euler=(z_out, z, u, dtr, w.tokens_per_row))
+
+    attn_ev = []
 
     def step(record):
-        def timed(name, fn):
-            if record:
-                a, bb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                fn()
-                bb.record()
-                ev[name].append((a, bb))
-            else:
-                fn()
-        timed("modulate", lambda: dit.dit_adaln_modulate(y, x, g, b, w.tokens_per_row, w.eps))
-        timed("rope", lambda: dit.dit_rope3d(q, k, grid, w.rope_split, w.rope_base, cu_seqlens=cu,
-                                             num_seqs=w.num_seqs))
-        if cu is None:
-            timed("attn", lambda: dit.dit_attn3d(o, q, k, v, num_seqs=w.num_seqs))
+        launch("modulate")
+        launch("rope")
+        if record:   # the dominant kernel, bracketed on the stream it runs on
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record()
+            launch("attn")
+            a1.record()
+            attn_ev.append((a0, a1))
         else:
-            timed("attn", lambda: dit.dit_attn3d(o, q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen))
-        timed("residual_euler", lambda: dit.dit_gated_residual(
-            x_out, x, o2d, al, w.tokens_per_row, euler=(z_out, z, u, dtr, w.tokens_per_row)))
+            launch("attn")
+        launch("residual_euler")
 
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
     print(f"[bench] {w.name}: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
 
-    # whole-step wall time: plain events around the K steps (no per-kernel events)
+    # timed region: K whole steps; the attention launches inside it carry their own events
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for _ in range(args.steps):
-        step(False)
+        step(True)
     t1.record()
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
+    kern_ms = {"attn": float(np.mean([a.elapsed_time(bb) for a, bb in attn_ev]))}
 
-    # per-kernel durations: events around each launch, on the launch stream
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    kern_ms = {n: float(np.mean([a.elapsed_time(bb) for a, bb in ev[n]])) for n in names}
+    # the short bandwidth-bound kernels: batches of back-to-back launches between two
+    # events (a single launch is too short for an event pair to time it faithfully),
+    # rotating over buffer copies worth >= 1 GiB so that no launch is served from the
+    # 256 MB last-level cache
+    def rotation(nbytes):
+        return max(2, min(16, -(-(1 << 30) // nbytes)))
+
+    def timed_batch(fns):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for f in fns:
+            f()
+        e0.record()
+        for _ in range(2):
+            for f in fns:
+                f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (2 * len(fns))
+
+    R = rotation(2 * w.tokens * w.d_model * esz)
+    xs = [x.clone() for _ in range(R)]
+    ys = [torch.empty_like(x) for _ in range(R)]
+    kern_ms["modulate"] = timed_batch([
+        (lambda i=i: dit.dit_adaln_modulate(ys[i], xs[i], g, b, w.tokens_per_row, w.eps)) for i in range(R)])
+    del ys
+    R = rotation(4 * w.tokens * w.d_model * esz)
+    qs = [q.clone() for _ in range(R)]
+    ks = [k.clone() for _ in range(R)]
+    kern_ms["rope"] = timed_batch([
+        (lambda i=i: dit.dit_rope3d(qs[i], ks[i], grid, w.rope_split, w.rope_base, cu_seqlens=cu,
+                                    num_seqs=w.num_seqs)) for i in range(R)])
+    del qs, ks
+    R = rotation(3 * w.tokens * w.d_model * esz)
+    xs = xs[:R] + [x.clone() for _ in range(R - len(xs))]
+    os_ = [o2d.clone() for _ in range(R)]
+    xo = [torch.empty_like(x) for _ in range(R)]
+    zs = [z.clone() for _ in range(R)]
+    us = [u.clone() for _ in range(R)]
+    zo = [torch.empty_like(z) for _ in range(R)]
+    kern_ms["residual_euler"] = timed_batch([
+        (lambda i=i: dit.dit_gated_residual(xo[i], xs[i], os_[i], al, w.tokens_per_row,
+                                            euler=(zo[i], zs[i], us[i], dtr, w.tokens_per_row)))
+        for i in range(R)])
+    del xs, os_, xo, zs, us, zo
 
     flops = w.attn_flops()
     tok, D, P = w.tokens, w.d_model, synth.LATENT_CHANNELS

@@ -60,11 +60,55 @@ __device__ __forceinline__ void load_f32x8(const float* base, int64_t idx8, floa
     f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-// Sum over the 64 lanes of a wave; every lane receives the total.
+// Sum over the 64 lanes of a wave; every lane receives the total. Lane exchanges
+// within each row of 16 lanes use DPP (quad_perm xor 1, xor 2, row_half_mirror,
+// row_mirror); the four row sums are then read with v_readlane.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
+
+// 8 activation values kept packed in registers (bf16: one uint4; fp32: two).
+template <bool BF16>
+struct Packed8;
+
+template <>
+struct Packed8<true> {
+    uint4 w;
+    __device__ __forceinline__ void load(const void* base, int64_t idx8) {
+        w = reinterpret_cast<const uint4*>(base)[idx8];
+    }
+    __device__ __forceinline__ void zero() { w = make_uint4(0, 0, 0, 0); }
+    // Empty asm that "redefines" the packed words: later passes unpack again
+    // instead of the compiler keeping all unpacked floats live (emits nothing).
+    __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w)); }
+    __device__ __forceinline__ void unpack(float (&f)[8]) const {
+        f[0] = bf16lo(w.x); f[1] = bf16hi(w.x); f[2] = bf16lo(w.y); f[3] = bf16hi(w.y);
+        f[4] = bf16lo(w.z); f[5] = bf16hi(w.z); f[6] = bf16lo(w.w); f[7] = bf16hi(w.w);
+    }
+};
+
+template <>
+struct Packed8<false> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const void* base, int64_t idx8) {
+        const float4* p = reinterpret_cast<const float4*>(base) + 2 * idx8;
+        a = p[0];
+        b = p[1];
+    }
+    __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ void refresh() {}
+    __device__ __forceinline__ void unpack(float (&f)[8]) const {
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    }
+};
 
 }  // namespace dit

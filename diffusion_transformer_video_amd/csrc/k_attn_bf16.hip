@@ -10,9 +10,11 @@
 //
 // Design
 //   * A block of NW waves owns 32*NW queries of one (sequence, head); each wave
-//     owns 32 queries. Blocks are numbered so that consecutive work items land
-//     on the same XCD (the dispatcher deals blocks round-robin over the 8 XCDs),
-//     which keeps the blocks that share one head's K/V on one L2.
+//     owns 32 queries. Work items are numbered head-major over the exact query
+//     tiles of all packed sequences (longest first) and remapped so that
+//     consecutive items land on the same XCD (the dispatcher deals blocks
+//     round-robin over the 8 XCDs): every XCD gets whole heads of every
+//     sequence, and its concurrent blocks share one head's K/V in its L2.
 //   * Scores are computed transposed, S^T = K Q^T (32 keys x 32 queries per
 //     MFMA tile). In the 32x32 accumulator layout a lane then holds 16 keys of a
 //     single query, so the row max/sum is a per-lane reduction plus one
@@ -323,28 +325,67 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a, int n
     __shared__ __attribute__((aligned(1024))) char kbuf[2][C::TILEB];
     __shared__ __attribute__((aligned(1024))) char vbuf[2][C::TILEB];
 
-    // ---- block -> (sequence, head, query tile), XCD-contiguous numbering
-    const int total = (int)gridDim.x;
-    const int b = (int)blockIdx.x;
-    const int per = total / 8, rem = total % 8;
-    const int xcd = b % 8, idx = b / 8;
-    const int w = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-    // the divisions run on the vector ALU; the results are block-uniform
-    const int qt = __builtin_amdgcn_readfirstlane(w % nqt);
-    const int head = __builtin_amdgcn_readfirstlane((w / nqt) % a.heads);
-    const int seq = __builtin_amdgcn_readfirstlane(w / (nqt * a.heads));
-
+    // ---- block -> (head, sequence, query tile)
+    // Work items are numbered head-major over the exact query tiles of every
+    // sequence (longest sequence first within a head), so that each XCD -- which
+    // receives a contiguous range of items -- gets whole heads with all their
+    // sequences (balanced) and its concurrent blocks share one head's K/V in L2.
+    // Blocks past the real total (the grid is sized for num_seqs x the longest
+    // sequence) are dealt last by the dispatcher and exit at once.
+    int total, seq, qt, head;
     int64_t s0;
     int len;
     if (a.cu_seqlens == nullptr) {
-        s0 = (int64_t)seq * a.max_seqlen;
-        len = a.max_seqlen;
+        total = (int)gridDim.x;
     } else {
-        // uniform per block: keep them in SGPRs so the buffer descriptors are scalar
-        const int c0 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq]);
-        const int c1 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq + 1]);
-        s0 = c0;
-        len = c1 - c0;
+        total = 0;
+        for (int s = 0; s < a.num_seqs; ++s) {
+            const int ls = __builtin_amdgcn_readfirstlane(a.cu_seqlens[s + 1] - a.cu_seqlens[s]);
+            total += (ls + C::BQ - 1) / C::BQ;
+        }
+        total *= a.heads;
+    }
+    const int b = (int)blockIdx.x;
+    if (b >= total) return;
+    {
+        const int per = total / 8, rem = total % 8;
+        const int xcd = b % 8, idx = b / 8;
+        const int w = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+        if (a.cu_seqlens == nullptr) {
+            const int per_head = nqt * a.num_seqs;
+            head = __builtin_amdgcn_readfirstlane(w / per_head);
+            const int r = w - head * per_head;
+            seq = __builtin_amdgcn_readfirstlane(r / nqt);
+            qt = __builtin_amdgcn_readfirstlane(r - seq * nqt);
+            s0 = (int64_t)seq * a.max_seqlen;
+            len = a.max_seqlen;
+        } else {
+            const int per_head = total / a.heads;
+            head = __builtin_amdgcn_readfirstlane(w / per_head);
+            int r = __builtin_amdgcn_readfirstlane(w - head * per_head);
+            // walk the sequences longest first (ties: lower index first); num_seqs is
+            // small, so the O(n^2) rank walk is a handful of scalar steps
+            seq = -1;
+            int prev_len = 0x7fffffff, prev_idx = -1;
+            for (int k = 0; k < a.num_seqs && seq < 0; ++k) {
+                // next sequence in (length desc, index asc) order after (prev_len, prev_idx)
+                int best = -1, best_len = -1;
+                for (int s = 0; s < a.num_seqs; ++s) {
+                    const int ls = __builtin_amdgcn_readfirstlane(a.cu_seqlens[s + 1] - a.cu_seqlens[s]);
+                    const bool after = a.num_seqs > 32 ? s > prev_idx   // many sequences: index order
+                                                       : ls < prev_len || (ls == prev_len && s > prev_idx);
+                    if (after && (a.num_seqs > 32 ? best < 0 : ls > best_len)) { best = s; best_len = ls; }
+                }
+                const int nt = (best_len + C::BQ - 1) / C::BQ;
+                if (r < nt) { seq = best; qt = r; } else { r -= nt; prev_len = best_len; prev_idx = best; }
+            }
+            seq = __builtin_amdgcn_readfirstlane(seq);
+            qt = __builtin_amdgcn_readfirstlane(qt);
+            const int c0 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq]);
+            const int c1 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq + 1]);
+            s0 = c0;
+            len = c1 - c0;
+        }
     }
     const int q0 = qt * C::BQ;
     if (q0 >= len) return;

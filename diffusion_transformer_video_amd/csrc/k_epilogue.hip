@@ -8,8 +8,9 @@
 //
 // Both are HBM-bound streams (6 bytes per bf16 element). The residual runs as
 // column strips: a thread owns one 8-column chunk and walks kTokPerThread
-// consecutive tokens, so the alpha chunk (a per-sample / per-frame row) is read
-// once per strip instead of once per element. The Euler part is a flat stream
+// consecutive tokens (all loads issued up front, kept in storage format), so the
+// alpha chunk (a per-sample / per-frame row) is read once per strip instead of
+// once per element; threads are numbered chunk-fastest over (strip, chunk). The Euler part is a flat stream
 // of 8-value chunks. In the fused launch the first blocks run the residual and
 // the remaining blocks the Euler update: two disjoint passes, one launch.
 #include "dit_device.hpp"
@@ -25,17 +26,19 @@ constexpr int kEulerChunksPerThread = 2;
 template <bool BF16>
 __device__ __forceinline__ void residual_block(const ResidualArgs& r, int64_t blk) {
     const int nchunk = r.d_model >> 3;
-    const int64_t col_blocks = (nchunk + kThreads - 1) / kThreads;
-    const int c = (int)(blk % col_blocks) * kThreads + (int)threadIdx.x;
-    const int64_t tok0 = (blk / col_blocks) * kTokPerThread;
-    if (c >= nchunk) return;
-    float xv[kTokPerThread][8], bv[kTokPerThread][8];
+    // flat index over (token group of kTokPerThread, column chunk), chunk fastest
+    const int64_t fi = blk * kThreads + threadIdx.x;
+    const int64_t ngroups = (r.tokens + kTokPerThread - 1) / kTokPerThread;
+    if (fi >= ngroups * nchunk) return;
+    const int c = (int)(fi % nchunk);
+    const int64_t tok0 = (fi / nchunk) * kTokPerThread;
+    Packed8<BF16> xv[kTokPerThread], bv[kTokPerThread];   // loads in flight, storage format
 #pragma unroll
     for (int t = 0; t < kTokPerThread; ++t) {
         const int64_t tok = tok0 + t;
         if (tok < r.tokens) {
-            Vec8<BF16>::load(r.x, tok * nchunk + c, xv[t]);
-            Vec8<BF16>::load(r.branch, tok * nchunk + c, bv[t]);
+            xv[t].load(r.x, tok * nchunk + c);
+            bv[t].load(r.branch, tok * nchunk + c);
         }
     }
     int64_t cur_row = -1;
@@ -49,9 +52,11 @@ __device__ __forceinline__ void residual_block(const ResidualArgs& r, int64_t bl
                 load_f32x8(r.alpha, row * nchunk + c, al);
                 cur_row = row;
             }
-            float o[8];
+            float xf[8], bf[8], o[8];
+            xv[t].unpack(xf);
+            bv[t].unpack(bf);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = fmaf(al[e], bv[t][e], xv[t][e]);
+            for (int e = 0; e < 8; ++e) o[e] = fmaf(al[e], bf[e], xf[e]);
             Vec8<BF16>::store(r.x_out, tok * nchunk + c, o);
         }
     }
@@ -62,13 +67,13 @@ __device__ __forceinline__ void euler_block(const EulerArgs& e, int64_t blk) {
     const int nchunk = e.channels >> 3;
     const int64_t total = e.tokens * nchunk;
     const int64_t base = blk * (kThreads * kEulerChunksPerThread) + threadIdx.x;
-    float zv[kEulerChunksPerThread][8], uv[kEulerChunksPerThread][8];
+    Packed8<BF16> zv[kEulerChunksPerThread], uv[kEulerChunksPerThread];
 #pragma unroll
     for (int i = 0; i < kEulerChunksPerThread; ++i) {
         const int64_t idx = base + (int64_t)i * kThreads;
         if (idx < total) {
-            Vec8<BF16>::load(e.z, idx, zv[i]);
-            Vec8<BF16>::load(e.u, idx, uv[i]);
+            zv[i].load(e.z, idx);
+            uv[i].load(e.u, idx);
         }
     }
 #pragma unroll
@@ -76,9 +81,11 @@ __device__ __forceinline__ void euler_block(const EulerArgs& e, int64_t blk) {
         const int64_t idx = base + (int64_t)i * kThreads;
         if (idx < total) {
             const float dt = e.dt_rows[(idx / nchunk) / e.tokens_per_row];
-            float o[8];
+            float zf[8], uf[8], o[8];
+            zv[i].unpack(zf);
+            uv[i].unpack(uf);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) o[k] = fmaf(dt, uv[i][k], zv[i][k]);
+            for (int k = 0; k < 8; ++k) o[k] = fmaf(dt, uf[k], zf[k]);
             Vec8<BF16>::store(e.z_out, idx, o);
         }
     }
@@ -86,9 +93,9 @@ __device__ __forceinline__ void euler_block(const EulerArgs& e, int64_t blk) {
 
 int64_t residual_blocks(const ResidualArgs* r) {
     if (r == nullptr || r->tokens == 0) return 0;
-    const int nchunk = r->d_model >> 3;
-    const int64_t col_blocks = (nchunk + kThreads - 1) / kThreads;
-    return col_blocks * ((r->tokens + kTokPerThread - 1) / kTokPerThread);
+    const int64_t nchunk = r->d_model >> 3;
+    const int64_t ngroups = (r->tokens + kTokPerThread - 1) / kTokPerThread;
+    return (ngroups * nchunk + kThreads - 1) / kThreads;
 }
 
 int64_t euler_blocks(const EulerArgs* e) {

@@ -5,10 +5,11 @@
 // equations). HBM-bound: one read of x, one write of y.
 //
 // One wave owns one token row. Each lane holds CPL chunks of 8 values in
-// registers (16-byte loads for bf16), so the row is read from HBM exactly once;
-// mean and variance are two exact passes over the registers with butterfly
-// wave reductions. gamma/beta rows are shared by every token of a sample/frame
-// and are served from cache.
+// registers in their storage format (bf16 stays packed: 4 VGPRs per 8 values,
+// which keeps occupancy high), so the row is read from HBM exactly once; mean
+// and variance are two exact passes over the registers with DPP wave
+// reductions. gamma/beta rows are shared by every token of a sample/frame and
+// are served from cache.
 #include "dit_device.hpp"
 #include "dit_internal.h"
 
@@ -28,31 +29,34 @@ __global__ __launch_bounds__(64 * kWaves) void modulate_kernel(
     const int nchunk = d_model >> 3;
     const int64_t row_chunk = tok * nchunk;
 
-    float v[CPL][8];
+    // the row stays in registers in its storage format (one HBM read)
+    Packed8<BF16> v[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = lane + 64 * i;
-        if (c < nchunk) {
-            Vec8<BF16>::load(x, row_chunk + c, v[i]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
-        }
+        if (c < nchunk) v[i].load(x, row_chunk + c); else v[i].zero();
     }
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i)
+    for (int i = 0; i < CPL; ++i) {
+        float f[8];
+        v[i].unpack(f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s += v[i][e];
+        for (int e = 0; e < 8; ++e) s += f[e];
+    }
     const float inv_d = 1.0f / (float)d_model;
     const float mean = wave_sum(s) * inv_d;
     float ss = 0.f;
 #pragma unroll
+    for (int i = 0; i < CPL; ++i) v[i].refresh();
+#pragma unroll
     for (int i = 0; i < CPL; ++i) {
         if (lane + 64 * i < nchunk) {
+            float f[8];
+            v[i].unpack(f);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float dlt = v[i][e] - mean;
+                const float dlt = f[e] - mean;
                 ss += dlt * dlt;
             }
         }
@@ -62,14 +66,17 @@ __global__ __launch_bounds__(64 * kWaves) void modulate_kernel(
 
     const int64_t prow = (tok / tokens_per_row) * nchunk;
 #pragma unroll
+    for (int i = 0; i < CPL; ++i) v[i].refresh();
+#pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = lane + 64 * i;
         if (c < nchunk) {
-            float g[8], b[8], o[8];
+            float f[8], g[8], b[8], o[8];
+            v[i].unpack(f);
             load_f32x8(gamma, prow + c, g);
             load_f32x8(beta, prow + c, b);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = fmaf(g[e], (v[i][e] - mean) * rstd, b[e]);
+            for (int e = 0; e < 8; ++e) o[e] = fmaf(g[e], (f[e] - mean) * rstd, b[e]);
             Vec8<BF16>::store(y, row_chunk + c, o);
         }
     }
