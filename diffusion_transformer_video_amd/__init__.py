@@ -19,7 +19,9 @@ import os
 from typing import Optional, Sequence
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdit.so")
+# DIT_LIB_PATH selects another build of the same library (e.g. an experiment);
+# by default the in-tree libdit.so next to this file is loaded
+LIB_PATH = os.environ.get("DIT_LIB_PATH") or os.path.join(_PKG, "libdit.so")
 
 DIT_F32, DIT_BF16 = 0, 1
 DIT_OK, DIT_E_INVAL, DIT_E_UNSUPPORTED, DIT_E_HIP = 0, 1, 2, 3

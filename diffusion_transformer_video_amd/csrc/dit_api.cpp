@@ -12,7 +12,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/dit.h"
+#include "dit.h"
 #include "dit_internal.h"
 
 namespace {

@@ -1,5 +1,7 @@
 // Device-side helpers shared by the gfx950 kernels: bf16 <-> fp32 packing,
-// 16-byte vector loads/stores of 8 activation values, and wave reductions.
+// 16-byte vector loads/stores of 8 activation values (stores are nontemporal:
+// every output of the bandwidth-bound kernels is written once and not re-read
+// by the same kernel), and wave reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,6 +10,8 @@
 namespace dit {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits.
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -34,7 +38,9 @@ struct Vec8<true> {
         uint4 w;
         w.x = pack_bf16x2(f[0], f[1]); w.y = pack_bf16x2(f[2], f[3]);
         w.z = pack_bf16x2(f[4], f[5]); w.w = pack_bf16x2(f[6], f[7]);
-        reinterpret_cast<uint4*>(base)[idx8] = w;
+        // streaming output: nontemporal store (not kept in the caches)
+        const u32x4 v = {w.x, w.y, w.z, w.w};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base) + idx8);
     }
 };
 
@@ -47,9 +53,11 @@ struct Vec8<false> {
         f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
     }
     __device__ __forceinline__ static void store(void* base, int64_t idx8, const float (&f)[8]) {
-        float4* p = reinterpret_cast<float4*>(base) + 2 * idx8;
-        p[0] = make_float4(f[0], f[1], f[2], f[3]);
-        p[1] = make_float4(f[4], f[5], f[6], f[7]);
+        f32x4* p = reinterpret_cast<f32x4*>(base) + 2 * idx8;
+        const f32x4 a = {f[0], f[1], f[2], f[3]};
+        const f32x4 b = {f[4], f[5], f[6], f[7]};
+        __builtin_nontemporal_store(a, p);
+        __builtin_nontemporal_store(b, p + 1);
     }
 };
 

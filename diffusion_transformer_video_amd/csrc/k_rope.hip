@@ -18,6 +18,7 @@ namespace dit {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kUnroll = 4;
 
 __device__ __forceinline__ void rotate8(float (&f)[8], const float (&cs)[4], const float (&sn)[4]) {
 #pragma unroll
@@ -79,18 +80,35 @@ __global__ __launch_bounds__(64 * kWaves) void rope3d_kernel(RopeArgs a) {
     }
 
     const int64_t tok_chunk = tok * (int64_t)a.heads * cph;
-    for (int h = hsub; h < a.heads; h += hpp) {
-        const int64_t idx = tok_chunk + (int64_t)h * cph + c;
-        float fq[8];
-        Vec8<BF16>::load(a.q, idx, fq);
-        if (a.k != nullptr) {
-            float fk[8];
-            Vec8<BF16>::load(a.k, idx, fk);
-            rotate8(fk, cs, sn);
-            Vec8<BF16>::store(a.k, idx, fk);
+    // kUnroll passes of the heads at a time: all their loads are issued before the
+    // first rotation, so each lane keeps 2 * kUnroll 16-byte loads in flight
+    for (int h0 = hsub; h0 < a.heads; h0 += kUnroll * hpp) {
+        Packed8<BF16> qv[kUnroll], kv[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int h = h0 + u * hpp;
+            if (h < a.heads) {
+                const int64_t idx = tok_chunk + (int64_t)h * cph + c;
+                qv[u].load(a.q, idx);
+                if (a.k != nullptr) kv[u].load(a.k, idx);
+            }
         }
-        rotate8(fq, cs, sn);
-        Vec8<BF16>::store(a.q, idx, fq);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int h = h0 + u * hpp;
+            if (h < a.heads) {
+                const int64_t idx = tok_chunk + (int64_t)h * cph + c;
+                float f[8];
+                qv[u].unpack(f);
+                rotate8(f, cs, sn);
+                Vec8<BF16>::store(a.q, idx, f);
+                if (a.k != nullptr) {
+                    kv[u].unpack(f);
+                    rotate8(f, cs, sn);
+                    Vec8<BF16>::store(a.k, idx, f);
+                }
+            }
+        }
     }
 }
 
