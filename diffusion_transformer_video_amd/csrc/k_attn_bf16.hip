@@ -59,8 +59,6 @@ constexpr float kLazyRescale = 8.0f;   // log2 headroom before the max is raised
 
 template <int HD, int NW>
 struct Cfg {
-    static constexpr int NT = 64 * NW;         // threads per block
-    static constexpr int BQ = 32 * NW;         // queries per block
     static constexpr int BK = 64;              // keys per tile
     static constexpr int ROWB = HD * 2;        // bytes per K / V row in LDS (no padding)
     static constexpr int CPR = HD / 8;         // 16-byte chunks per row
@@ -68,6 +66,10 @@ struct Cfg {
     static constexpr int TILEB = BK * ROWB;    // bytes of one K (or V) tile
     static constexpr int NBLK = TILEB / 1024;  // 1 KB blocks per tile
     static constexpr int LPW = NBLK / NW;      // block loads per wave per tile
+    // LDS ring depth per stream: with 8 waves (one block per CU) three K and three V
+    // tiles fit (96 KB) and both streams run two tiles ahead; with 4 waves (two
+    // blocks per CU) two of each (64 KB per block) and one tile ahead.
+    static constexpr int ST = NW >= 8 ? 3 : 2;
     static constexpr int NKK = HD / 16;        // k-steps of the S^T product
     static constexpr int NDT = HD / 32;        // 32-wide d tiles of O^T
     static_assert(LPW >= 1 && LPW * NW == NBLK, "tile loads must split evenly over the waves");
@@ -133,6 +135,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(lds_ptr_t)(const_cast<void*>(p));   // LDS byte address
 }
 
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 16-byte LDS read at byte address a + OFF (OFF folds into the instruction)
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t a) {
+    return *(lds_bf16x8*)(uintptr_t)(a + OFF);
+}
+
 // Direct global->LDS loads of one K or V tile (keys kbase..kbase+63 of the
 // sequence) into the LDS tile at `dst`. Wave w moves 1 KB blocks w, w+NW, ...; in
 // a block, lane L carries row RPB*blk + L/CPR at physical chunk L%CPR, i.e. the
@@ -171,30 +182,74 @@ __device__ __forceinline__ void issue_any(const i32x4& rs, const char* dst, int 
         issue<HD, NW, false, ISV>(rs, dst, wave, lane, ldb, kbase, len - kbase, off);
 }
 
-// S^T tile = K Q^T from LDS K tile `kb` (two 32-key blocks). kaddr[kk]: this
-// lane's K operand offset (row l32, logical chunk 2kk + g).
+// K operands of one tile: for k-step kk and key block kb, this lane's 16 bytes
+// (row 32kb + l32, logical chunk 2kk + g). All are read up front so their LDS
+// latency hides behind the softmax of the previous tile.
 template <int HD, int NW>
-__device__ __forceinline__ void s_tile(const char* kb, const int (&kaddr)[Cfg<HD, NW>::NKK],
-                                       const bf16x8 (&qreg)[Cfg<HD, NW>::NKK], f32x16& S0, f32x16& S1) {
+__device__ __forceinline__ void k_fetch(uint32_t kb, const int (&kaddr)[Cfg<HD, NW>::NKK],
+                                        bf16x8 (&ka)[2 * Cfg<HD, NW>::NKK]) {
     using C = Cfg<HD, NW>;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { S0[r] = 0.f; S1[r] = 0.f; }
+    for (int kk = 0; kk < C::NKK; ++kk) {
+        const uint32_t a = kb + kaddr[kk];
+        ka[2 * kk] = lds_read16<0>(a);
+        ka[2 * kk + 1] = lds_read16<32 * C::ROWB>(a);
+    }
+}
+
+// S^T = K Q^T for both 32-key blocks and all QB query blocks of this wave: each
+// K operand read from LDS feeds QB products.
+template <int HD, int NW, int QB>
+__device__ __forceinline__ void s_mfma(const bf16x8 (&ka)[2 * Cfg<HD, NW>::NKK],
+                                       const bf16x8 (&qreg)[QB][Cfg<HD, NW>::NKK], f32x16 (&S)[QB][2]) {
+    using C = Cfg<HD, NW>;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { S[qb][0][r] = 0.f; S[qb][1][r] = 0.f; }
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            S[qb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[2 * kk], qreg[qb][kk], S[qb][0], 0, 0, 0);
+            S[qb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[2 * kk + 1], qreg[qb][kk], S[qb][1], 0, 0, 0);
+        }
+}
+
+// S^T as above with the K operands read from LDS just before use (no prefetch
+// registers; with QB = 2 every read already feeds two products).
+template <int HD, int NW, int QB>
+__device__ __forceinline__ void s_tile(uint32_t kb, const int (&kaddr)[Cfg<HD, NW>::NKK],
+                                       const bf16x8 (&qreg)[QB][Cfg<HD, NW>::NKK], f32x16 (&S)[QB][2]) {
+    using C = Cfg<HD, NW>;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { S[qb][0][r] = 0.f; S[qb][1][r] = 0.f; }
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kb + kaddr[kk]);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kb + kaddr[kk] + 32 * C::ROWB);
-        S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], S0, 0, 0, 0);
-        S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], S1, 0, 0, 0);
+        const uint32_t a = kb + kaddr[kk];
+        const bf16x8 a0 = lds_read16<0>(a);
+        const bf16x8 a1 = lds_read16<32 * C::ROWB>(a);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            S[qb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[qb][kk], S[qb][0], 0, 0, 0);
+            S[qb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[qb][kk], S[qb][1], 0, 0, 0);
+        }
     }
 }
 
 // Keys >= len of the tile starting at kbase get score -inf (last tile only).
-__device__ __forceinline__ void mask_tile(f32x16& S0, f32x16& S1, int g, int kbase, int len) {
+template <int QB>
+__device__ __forceinline__ void mask_tile(f32x16 (&S)[QB][2], int g, int kbase, int len) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int k = kbase + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (k >= len) S0[r] = -INFINITY;
-        if (k + 32 >= len) S1[r] = -INFINITY;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            if (k >= len) S[qb][0][r] = -INFINITY;
+            if (k + 32 >= len) S[qb][1][r] = -INFINITY;
+        }
     }
 }
 
@@ -205,8 +260,9 @@ __device__ __forceinline__ float max16(const f32x16& S) {
     return __builtin_fmaxf(mx, S[15]);
 }
 
-// Online-softmax bookkeeping of one tile: raise the running max (and rescale O
-// and l) only if the tile max exceeds it by more than 2^kLazyRescale.
+// Online-softmax bookkeeping of one tile for one query block: raise the running
+// max (and rescale O and l) only if the tile max exceeds it by more than
+// 2^kLazyRescale.
 template <int NDT>
 __device__ __forceinline__ void tile_max_update(const f32x16& S0, const f32x16& S1, f32x16 (&O)[NDT],
                                                 float& m_run, float& l_run, float c) {
@@ -238,32 +294,49 @@ __device__ __forceinline__ bf16x8 probs8(const f32x16& S, int t, float c, float 
     return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
-// V^T operand for one MFMA step: 4 consecutive keys at vaddr and 4 more 8 keys
-// later (the two halves of the lane's 8 contraction slots), transposed on read.
-__device__ __forceinline__ bf16x8 vt_operand(const char* vaddr, int second) {
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vaddr));
-    const s16x4 hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vaddr + second));
+// V^T operand for one MFMA step: 4 consecutive keys at byte address a + OFF and 4
+// more 8 keys (SECOND bytes) later -- the two halves of the lane's 8 contraction
+// slots -- transposed on read.
+template <int OFF, int SECOND>
+__device__ __forceinline__ bf16x8 vt_operand(uint32_t a) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(a + OFF));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(a + OFF + SECOND));
     const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// O^T += V^T P^T for one 16-key MFMA step (kb, t) of a tile. vaddr[dt]: this
-// lane's V^T source offset for d tile dt, first step; step (kb, t) adds
-// 32kb + 16t rows.
-template <int HD, int NW>
-__device__ __forceinline__ void pv_step(const char* vb, const int (&vaddr)[Cfg<HD, NW>::NDT], int kb,
-                                        int t, const bf16x8& P, f32x16 (&O)[Cfg<HD, NW>::NDT]) {
+// O^T += V^T P^T for one 16-key MFMA step (KB, T) of a tile, for every query block:
+// each V^T operand read from LDS feeds QB products. vb[dt]: this lane's V^T source
+// address for d tile dt, first step, in the current V tile; step (KB, T) adds
+// 32 KB + 16 T rows (a constant offset).
+template <int HD, int NW, int QB, int KB, int T>
+__device__ __forceinline__ void pv_step(const uint32_t (&vb)[Cfg<HD, NW>::NDT], const bf16x8 (&P)[QB][4],
+                                        f32x16 (&O)[QB][Cfg<HD, NW>::NDT]) {
     using C = Cfg<HD, NW>;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) {
-        const bf16x8 v = vt_operand(vb + vaddr[dt] + (32 * kb + 16 * t) * C::ROWB, 8 * C::ROWB);
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, P, O[dt], 0, 0, 0);
+        const bf16x8 v = vt_operand<(32 * KB + 16 * T) * C::ROWB, 8 * C::ROWB>(vb[dt]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            O[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, P[qb][2 * KB + T], O[qb][dt], 0, 0, 0);
     }
 }
 
+template <int HD, int NW, int QB>
+__device__ __forceinline__ void pv_tile(uint32_t vread, const int (&vaddr)[Cfg<HD, NW>::NDT],
+                                        const bf16x8 (&P)[QB][4], f32x16 (&O)[QB][Cfg<HD, NW>::NDT]) {
+    using C = Cfg<HD, NW>;
+    uint32_t vb[C::NDT];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) vb[dt] = vread + vaddr[dt];
+    pv_step<HD, NW, QB, 0, 0>(vb, P, O);
+    pv_step<HD, NW, QB, 0, 1>(vb, P, O);
+    pv_step<HD, NW, QB, 1, 0>(vb, P, O);
+    pv_step<HD, NW, QB, 1, 1>(vb, P, O);
+}
+
 // Per-block state threaded through the pipeline.
-template <int HD, int NW>
+template <int HD, int NW, int QB>
 struct Pipe {
     using C = Cfg<HD, NW>;
     i32x4 rk, rv;
@@ -271,59 +344,94 @@ struct Pipe {
     uint32_t ldb, koff, voff;
     int kaddr[C::NKK];
     int vaddr[C::NDT];
-    bf16x8 qreg[C::NKK];
-    f32x16 O[C::NDT];
-    float m_run, l_run, c;
+    bf16x8 qreg[QB][C::NKK];
+    f32x16 O[QB][C::NDT];
+    float m_run[QB], l_run[QB];
+    float c;
 };
 
-// One pipeline step for tile j (S = S(j) in registers): stream K(j+2) into kdma
-// and V(j+1) into vdma, softmax of S(j) || S(j+1) = K(j+1) Q^T from kread, then
-// O += V(j) P(j) from vread. Requires j+1 < ntiles.
-template <int HD, int NW>
-__device__ __forceinline__ void pipe_step(Pipe<HD, NW>& p, int j, f32x16& S0, f32x16& S1,
-                                          const char* kread, const char* kdma, const char* vread,
-                                          const char* vdma) {
+// Softmax of the tile held in S: running-max update and the bf16 probabilities
+// P[qb][2kb + t] for each query block.
+template <int HD, int NW, int QB>
+__device__ __forceinline__ void softmax_tile(Pipe<HD, NW, QB>& p, const f32x16 (&S)[QB][2],
+                                             bf16x8 (&P)[QB][4]) {
     using C = Cfg<HD, NW>;
-    if (j + 2 < p.ntiles)
-        issue_any<HD, NW, false>(p.rk, kdma, p.wave, p.lane, p.ldb, (uint32_t)(j + 2) * C::BK,
-                                 (uint32_t)p.len, p.koff);
-    issue_any<HD, NW, true>(p.rv, vdma, p.wave, p.lane, p.ldb, (uint32_t)(j + 1) * C::BK, (uint32_t)p.len,
-                            p.voff);
-    tile_max_update<C::NDT>(S0, S1, p.O, p.m_run, p.l_run, p.c);
-    const bf16x8 P00 = probs8(S0, 0, p.c, p.m_run, p.l_run);
-    const bf16x8 P01 = probs8(S0, 1, p.c, p.m_run, p.l_run);
-    const bf16x8 P10 = probs8(S1, 0, p.c, p.m_run, p.l_run);
-    const bf16x8 P11 = probs8(S1, 1, p.c, p.m_run, p.l_run);
-    s_tile<HD, NW>(kread, p.kaddr, p.qreg, S0, S1);   // S(j+1): independent of the exps above
-    pv_step<HD, NW>(vread, p.vaddr, 0, 0, P00, p.O);
-    pv_step<HD, NW>(vread, p.vaddr, 0, 1, P01, p.O);
-    pv_step<HD, NW>(vread, p.vaddr, 1, 0, P10, p.O);
-    pv_step<HD, NW>(vread, p.vaddr, 1, 1, P11, p.O);
-    if (j + 1 == p.ntiles - 1) mask_tile(S0, S1, p.g, (j + 1) * C::BK, p.len);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads have landed in LDS
-    __syncthreads();                                     // ... and everyone's; all reads of tile j done
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        tile_max_update<C::NDT>(S[qb][0], S[qb][1], p.O[qb], p.m_run[qb], p.l_run[qb], p.c);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) P[qb][2 * kb + t] = probs8(S[qb][kb], t, p.c, p.m_run[qb], p.l_run[qb]);
+    }
 }
 
-// Final tile (S = S(j) in registers, V(j) in vread).
-template <int HD, int NW>
-__device__ __forceinline__ void pipe_last(Pipe<HD, NW>& p, f32x16& S0, f32x16& S1, const char* vread) {
+// One pipeline step for tile j (S = S(j) in registers; K(j+1) and V(j) resident):
+// stream K(j+ST) and V(j+ST-1) into their ring slots, softmax of S(j) ||
+// S(j+1) = K(j+1) Q^T, then O += V(j) P(j); finally wait for the tiles the next
+// step needs and publish them with a barrier. Requires j+1 < ntiles.
+template <int HD, int NW, int QB>
+__device__ __forceinline__ void pipe_step(Pipe<HD, NW, QB>& p, int j, f32x16 (&S)[QB][2], char* kring,
+                                          char* vring) {
     using C = Cfg<HD, NW>;
-    tile_max_update<C::NDT>(S0, S1, p.O, p.m_run, p.l_run, p.c);
-    const bf16x8 P00 = probs8(S0, 0, p.c, p.m_run, p.l_run);
-    const bf16x8 P01 = probs8(S0, 1, p.c, p.m_run, p.l_run);
-    const bf16x8 P10 = probs8(S1, 0, p.c, p.m_run, p.l_run);
-    const bf16x8 P11 = probs8(S1, 1, p.c, p.m_run, p.l_run);
-    pv_step<HD, NW>(vread, p.vaddr, 0, 0, P00, p.O);
-    pv_step<HD, NW>(vread, p.vaddr, 0, 1, P01, p.O);
-    pv_step<HD, NW>(vread, p.vaddr, 1, 0, P10, p.O);
-    pv_step<HD, NW>(vread, p.vaddr, 1, 1, P11, p.O);
+    const int kn = j + C::ST, vn = j + C::ST - 1;   // tiles streamed in this step
+    const bool issue_k = kn < p.ntiles, issue_v = vn < p.ntiles;
+    if (issue_k)
+        issue_any<HD, NW, false>(p.rk, kring + (kn % C::ST) * C::TILEB, p.wave, p.lane, p.ldb,
+                                 (uint32_t)kn * C::BK, (uint32_t)p.len, p.koff);
+    if (issue_v)
+        issue_any<HD, NW, true>(p.rv, vring + (vn % C::ST) * C::TILEB, p.wave, p.lane, p.ldb,
+                                (uint32_t)vn * C::BK, (uint32_t)p.len, p.voff);
+    // ring slot bases as opaque scalars: otherwise loop strength reduction turns
+    // every lane address into its own induction variable with a wrap correction
+    const uint32_t kread = __builtin_amdgcn_readfirstlane(lds_addr(kring) + ((j + 1) % C::ST) * C::TILEB);
+    const uint32_t vread = __builtin_amdgcn_readfirstlane(lds_addr(vring) + (j % C::ST) * C::TILEB);
+    bf16x8 P[QB][4];
+    if constexpr (QB == 1 && NW == 4) {   // registers to spare: read all K operands first
+        bf16x8 ka[2 * C::NKK];
+        k_fetch<HD, NW>(kread, p.kaddr, ka);
+        softmax_tile<HD, NW, QB>(p, S, P);
+        s_mfma<HD, NW, QB>(ka, p.qreg, S);   // S(j+1): independent of the exps above
+    } else {
+        softmax_tile<HD, NW, QB>(p, S, P);
+        s_tile<HD, NW, QB>(kread, p.kaddr, p.qreg, S);   // S(j+1): independent of the exps above
+    }
+    pv_tile<HD, NW, QB>(vread, p.vaddr, P, p.O);
+    if (j + 1 == p.ntiles - 1) mask_tile<QB>(S, p.g, (j + 1) * C::BK, p.len);
+    // the next step reads K(j+2) and V(j+1): with a 2-deep ring they were issued in
+    // this step, with a 3-deep ring in the previous one, so this step's own loads
+    // (completing in issue order) may stay in flight
+    if constexpr (C::ST == 2) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+        static_assert(C::LPW == 2, "3-deep ring wait counts assume two loads per stream per wave");
+        if (issue_k)
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else if (issue_v)
+            asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();   // everyone's loads have landed; all reads of tile j are done
 }
 
-template <int HD, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a, int nqt) {
+// Final tile (S = S(j) in registers, V(j) at LDS address vread).
+template <int HD, int NW, int QB>
+__device__ __forceinline__ void pipe_last(Pipe<HD, NW, QB>& p, const f32x16 (&S)[QB][2], uint32_t vread) {
+    bf16x8 P[QB][4];
+    softmax_tile<HD, NW, QB>(p, S, P);
+    pv_tile<HD, NW, QB>(vread, p.vaddr, P, p.O);
+}
+
+// QB = query blocks of 32 per wave. QB = 2 halves the LDS operand traffic per
+// flop but needs about 450 registers, i.e. one wave per SIMD (VGPRs + AGPRs);
+// QB = 1 runs two waves per SIMD.
+template <int HD, int NW, int QB>
+__global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf16_kernel(AttnArgs a, int nqt) {
     using C = Cfg<HD, NW>;
-    __shared__ __attribute__((aligned(1024))) char kbuf[2][C::TILEB];
-    __shared__ __attribute__((aligned(1024))) char vbuf[2][C::TILEB];
+    constexpr int BQ = 32 * QB * NW;   // queries per block
+    __shared__ __attribute__((aligned(1024))) char kbuf[C::ST][C::TILEB];
+    __shared__ __attribute__((aligned(1024))) char vbuf[C::ST][C::TILEB];
 
     // ---- block -> (head, sequence, query tile)
     // Work items are numbered head-major over the exact query tiles of every
@@ -341,7 +449,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a, int n
         total = 0;
         for (int s = 0; s < a.num_seqs; ++s) {
             const int ls = __builtin_amdgcn_readfirstlane(a.cu_seqlens[s + 1] - a.cu_seqlens[s]);
-            total += (ls + C::BQ - 1) / C::BQ;
+            total += (ls + BQ - 1) / BQ;
         }
         total *= a.heads;
     }
@@ -376,7 +484,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a, int n
                                                        : ls < prev_len || (ls == prev_len && s > prev_idx);
                     if (after && (a.num_seqs > 32 ? best < 0 : ls > best_len)) { best = s; best_len = ls; }
                 }
-                const int nt = (best_len + C::BQ - 1) / C::BQ;
+                const int nt = (best_len + BQ - 1) / BQ;
                 if (r < nt) { seq = best; qt = r; } else { r -= nt; prev_len = best_len; prev_idx = best; }
             }
             seq = __builtin_amdgcn_readfirstlane(seq);
@@ -387,10 +495,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a, int n
             len = c1 - c0;
         }
     }
-    const int q0 = qt * C::BQ;
+    const int q0 = qt * BQ;
     if (q0 >= len) return;
 
-    Pipe<HD, NW> p;
+    Pipe<HD, NW, QB> p;
     const int tid = threadIdx.x;
     p.lane = tid & 63;
     p.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -430,71 +538,90 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16_kernel(AttnArgs a, int n
         }
     }
 
-    // ---- Q (B operand of S^T = K Q^T): lane holds query l32, d = 16kk + 8g .. +7
-    const int my_q = q0 + p.wave * 32 + l32;
-    const uint32_t qrow = (uint32_t)(my_q < len ? my_q : len - 1);
+    // ---- Q (B operand of S^T = K Q^T): block qb of this wave, lane holds query
+    // q0 + 32(QB wave + qb) + l32, d = 16kk + 8g .. +7
+    int my_q[QB];
 #pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk)
-        p.qreg[kk] = __builtin_bit_cast(bf16x8, bload(rq, qrow * p.ldb + (2 * kk + p.g) * 16, 0));
+    for (int qb = 0; qb < QB; ++qb) {
+        my_q[qb] = q0 + 32 * (QB * p.wave + qb) + l32;
+        const uint32_t qrow = (uint32_t)(my_q[qb] < len ? my_q[qb] : len - 1);
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
+        for (int kk = 0; kk < C::NKK; ++kk)
+            p.qreg[qb][kk] = __builtin_bit_cast(bf16x8, bload(rq, qrow * p.ldb + (2 * kk + p.g) * 16, 0));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p.O[dt][r] = 0.f;
-    p.m_run = -INFINITY;   // running max in the scaled log2 domain
-    p.l_run = 0.f;         // this lane's partial row sum (its 16 keys per tile)
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p.O[qb][dt][r] = 0.f;
+        p.m_run[qb] = -INFINITY;   // running max in the scaled log2 domain
+        p.l_run[qb] = 0.f;         // this lane's partial row sum (its 16 keys per tile)
+    }
     p.c = a.scale_log2;
 
-    // ---- prologue: K(0), V(0), K(1) in flight; S(0)
+    // ---- prologue: K(0), V(0), K(1) resident; S(0); then the loads a step -1
+    // would have issued (K(ST-1), V(ST-2)) for a 3-deep ring
     issue_any<HD, NW, false>(p.rk, kbuf[0], p.wave, p.lane, p.ldb, 0, (uint32_t)len, p.koff);
     issue_any<HD, NW, true>(p.rv, vbuf[0], p.wave, p.lane, p.ldb, 0, (uint32_t)len, p.voff);
     if (p.ntiles > 1)
         issue_any<HD, NW, false>(p.rk, kbuf[1], p.wave, p.lane, p.ldb, C::BK, (uint32_t)len, p.koff);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    f32x16 S0, S1;
-    s_tile<HD, NW>(kbuf[0], p.kaddr, p.qreg, S0, S1);
-    if (p.ntiles == 1) mask_tile(S0, S1, p.g, 0, len);
+    f32x16 S[QB][2];
+    {
+        bf16x8 ka[2 * C::NKK];
+        k_fetch<HD, NW>(lds_addr(kbuf[0]), p.kaddr, ka);
+        s_mfma<HD, NW, QB>(ka, p.qreg, S);
+    }
+    if (p.ntiles == 1) mask_tile<QB>(S, p.g, 0, len);
+    // every wave's reads of K(0) are done before step 0 streams into its slot
+    __syncthreads();
+    if constexpr (C::ST == 3) {
+        if (p.ntiles > 2)
+            issue_any<HD, NW, false>(p.rk, kbuf[2], p.wave, p.lane, p.ldb, 2 * C::BK, (uint32_t)len, p.koff);
+        if (p.ntiles > 1)
+            issue_any<HD, NW, true>(p.rv, vbuf[1], p.wave, p.lane, p.ldb, C::BK, (uint32_t)len, p.voff);
+    }
 
-    // ---- steady state: tile j uses K(j+1) in kbuf[(j+1)&1], V(j) in vbuf[j&1];
-    // K(j+2) streams into kbuf[j&1], V(j+1) into vbuf[(j+1)&1]
-    for (int j = 0; j + 1 < p.ntiles; ++j)
-        pipe_step<HD, NW>(p, j, S0, S1, kbuf[(j + 1) & 1], kbuf[j & 1], vbuf[j & 1], vbuf[(j + 1) & 1]);
-    pipe_last<HD, NW>(p, S0, S1, vbuf[(p.ntiles - 1) & 1]);
+    // ---- steady state: step j reads K(j+1), V(j) from ring slots (j+1) % ST, j % ST
+    for (int j = 0; j + 1 < p.ntiles; ++j) pipe_step<HD, NW, QB>(p, j, S, kbuf[0], vbuf[0]);
+    pipe_last<HD, NW, QB>(p, S, lds_addr(vbuf[0]) + ((p.ntiles - 1) % C::ST) * C::TILEB);
 
-    // ---- normalise and store: lane holds query l32, d = 32dt + 8(r/4) + 4g + r%4
-    const float inv = 1.0f / pair_sum(p.l_run);   // lanes l and l^32 summed disjoint keys
-    if (my_q < len) {
-        uint2* Og = reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(a.o) + base +
-                                             (int64_t)my_q * a.heads * HD);
+    // ---- normalise and store: lane holds query my_q[qb], d = 32dt + 8(r/4) + 4g + r%4
 #pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) {
+    for (int qb = 0; qb < QB; ++qb) {
+        const float inv = 1.0f / pair_sum(p.l_run[qb]);   // lanes l and l^32 summed disjoint keys
+        if (my_q[qb] < len) {
+            uint2* Og = reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(a.o) + base +
+                                                 (int64_t)my_q[qb] * a.heads * HD);
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                uint2 wv;
-                wv.x = pack_bf16x2(p.O[dt][4 * rg + 0] * inv, p.O[dt][4 * rg + 1] * inv);
-                wv.y = pack_bf16x2(p.O[dt][4 * rg + 2] * inv, p.O[dt][4 * rg + 3] * inv);
-                Og[(dt * 32 + 8 * rg + 4 * p.g) / 4] = wv;
+            for (int dt = 0; dt < C::NDT; ++dt) {
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    uint2 wv;
+                    wv.x = pack_bf16x2(p.O[qb][dt][4 * rg + 0] * inv, p.O[qb][dt][4 * rg + 1] * inv);
+                    wv.y = pack_bf16x2(p.O[qb][dt][4 * rg + 2] * inv, p.O[qb][dt][4 * rg + 3] * inv);
+                    Og[(dt * 32 + 8 * rg + 4 * p.g) / 4] = wv;
+                }
             }
         }
     }
 }
 
-template <int HD, int NW>
+template <int HD, int NW, int QB>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
-    using C = Cfg<HD, NW>;
-    const int nqt = (a.max_seqlen + C::BQ - 1) / C::BQ;
+    constexpr int BQ = 32 * QB * NW;
+    const int nqt = (a.max_seqlen + BQ - 1) / BQ;
     const int64_t total = (int64_t)nqt * a.heads * a.num_seqs;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_bf16_kernel<HD, NW>), dim3((unsigned)total), dim3(C::NT), 0, s, a, nqt);
+    hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, QB>), dim3((unsigned)total), dim3(64 * NW), 0, s, a, nqt);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn3d_bf16(const AttnArgs& a, hipStream_t s) {
-    if (a.head_dim == 64) return launch_t<64, 4>(a, s);
-    return launch_t<128, 4>(a, s);
+    if (a.head_dim == 64) return launch_t<64, 4, 1>(a, s);
+    return launch_t<128, 8, 1>(a, s);
 }
 
 }  // namespace dit
