@@ -8,8 +8,11 @@
 // registers in their storage format (bf16 stays packed: 4 VGPRs per 8 values,
 // which keeps occupancy high), so the row is read from HBM exactly once; mean
 // and variance are two exact passes over the registers with DPP wave
-// reductions. gamma/beta rows are shared by every token of a sample/frame and
-// are served from cache.
+// reductions. gamma/beta rows are shared by every token of a sample/frame: for
+// wide bf16 rows a block of kWavesL waves (kWavesL consecutive tokens) stages the
+// parameter row it shares in LDS once, so the parameter rows leave the cache
+// once per kWavesL tokens instead of once per token; elsewhere they are served
+// from cache per token.
 #include "dit_device.hpp"
 #include "dit_internal.h"
 
@@ -82,10 +85,122 @@ __global__ __launch_bounds__(64 * kWaves) void modulate_kernel(
     }
 }
 
+constexpr int kWavesL = 8;
+
+// Same per-row arithmetic as modulate_kernel; gamma/beta of the block's tokens
+// come from LDS when all kWavesL tokens use one parameter row (decided per
+// block, so the branch is uniform), else from global memory per token. The x
+// loads are issued before the staging loads and the barrier, so they overlap.
+template <bool BF16, int CPL>
+__global__ __launch_bounds__(64 * kWavesL) void modulate_lds_kernel(
+    void* __restrict__ y, const void* __restrict__ x, const float* __restrict__ gamma,
+    const float* __restrict__ beta, int64_t tokens, int d_model, int64_t tokens_per_row,
+    float eps) {
+    extern __shared__ float4 gb_lds[];   // [2][d_model / 4]: gamma then beta
+    const int lane = threadIdx.x & 63;
+    const int64_t tok0 = (int64_t)blockIdx.x * kWavesL;
+    const int64_t tok = tok0 + (threadIdx.x >> 6);
+    const int nchunk = d_model >> 3;
+    const int64_t row_chunk = tok * nchunk;
+    const bool live = tok < tokens;
+
+    Packed8<BF16> v[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        if (live && c < nchunk) v[i].load(x, row_chunk + c); else v[i].zero();
+    }
+    const int64_t last = (tok0 + kWavesL < tokens ? tok0 + kWavesL : tokens) - 1;
+    const int64_t prow0 = tok0 / tokens_per_row;
+    const bool shared_row = (last / tokens_per_row) == prow0;
+    if (shared_row) {
+        const float4* g4 = reinterpret_cast<const float4*>(gamma + prow0 * d_model);
+        const float4* b4 = reinterpret_cast<const float4*>(beta + prow0 * d_model);
+        const int n4 = d_model >> 2;
+        for (int i = threadIdx.x; i < n4; i += 64 * kWavesL) {
+            gb_lds[i] = g4[i];
+            gb_lds[n4 + i] = b4[i];
+        }
+    }
+    __syncthreads();
+    if (!live) return;
+
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        float f[8];
+        v[i].unpack(f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += f[e];
+    }
+    const float inv_d = 1.0f / (float)d_model;
+    const float mean = wave_sum(s) * inv_d;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) v[i].refresh();
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        if (lane + 64 * i < nchunk) {
+            float f[8];
+            v[i].unpack(f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float dlt = f[e] - mean;
+                ss += dlt * dlt;
+            }
+        }
+    }
+    const float var = wave_sum(ss) * inv_d;
+    const float rstd = 1.0f / sqrtf(var + eps);
+    const int64_t prow = tok / tokens_per_row;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) v[i].refresh();
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nchunk) {
+            float f[8], g[8], b[8], o[8];
+            v[i].unpack(f);
+            if (shared_row) {
+                const float4 g0 = gb_lds[2 * c], g1 = gb_lds[2 * c + 1];
+                const float4 b0 = gb_lds[2 * nchunk + 2 * c], b1 = gb_lds[2 * nchunk + 2 * c + 1];
+                g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+                g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+                b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w;
+                b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+            } else {
+                load_f32x8(gamma, prow * nchunk + c, g);
+                load_f32x8(beta, prow * nchunk + c, b);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = fmaf(g[e], (f[e] - mean) * rstd, b[e]);
+            Vec8<BF16>::store(y, row_chunk + c, o);
+        }
+    }
+}
+
 template <bool BF16>
 hipError_t launch_t(const ModulateArgs& a, hipStream_t s) {
     const int nchunk = a.d_model / 8;
     const int cpl = (nchunk + 63) / 64;
+    if constexpr (BF16) if (nchunk >= 256) {   // rows of 2048+ bf16 values: LDS-staged parameters
+        const dim3 grid((unsigned)((a.tokens + kWavesL - 1) / kWavesL));
+        const size_t lds = (size_t)a.d_model * 2 * sizeof(float);   // <= 64 KB
+#define DIT_MODL_CASE(N)                                                                          \
+        if (cpl <= N) {                                                                           \
+            hipLaunchKernelGGL((modulate_lds_kernel<BF16, N>), grid, dim3(64 * kWavesL), lds, s,  \
+                               a.y, a.x, a.gamma, a.beta, a.tokens, a.d_model, a.tokens_per_row, \
+                               a.eps);                                                            \
+            return hipGetLastError();                                                             \
+        }
+        DIT_MODL_CASE(4)
+        DIT_MODL_CASE(6)
+        DIT_MODL_CASE(8)
+        DIT_MODL_CASE(10)
+        DIT_MODL_CASE(12)
+        DIT_MODL_CASE(16)
+#undef DIT_MODL_CASE
+    }
     const dim3 grid((unsigned)((a.tokens + kWaves - 1) / kWaves));
     const dim3 block(64 * kWaves);
 #define DIT_MOD_CASE(N)                                                                     \

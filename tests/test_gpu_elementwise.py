@@ -48,6 +48,22 @@ def test_modulate_small(w):
     _modulate_case(w)
 
 
+# wide bf16 rows (2048+ values): parameter rows staged once per block of 8 tokens;
+# these also cover a block whose tokens straddle two parameter rows (rows of 15
+# tokens), a partial last block (90 tokens), a row width that leaves lanes idle
+# (2056 = 257 chunks of 8) and the widest supported row (8192)
+WIDE = [
+    synth.custom("wide2048_rows15", "bf16", (3, 5), (3, 1, 2), 16, 128, (44, 42, 42), tokens_per_row=15),
+    synth.custom("wide2056_ragged", "bf16", (2, 7), (3,), 257, 8, (4, 2, 2), tokens_per_row=7),
+    synth.custom("wide8192", "bf16", (4, 5), (2,), 64, 128, (44, 42, 42), tokens_per_row=20),
+]
+
+
+@pytest.mark.parametrize("w", WIDE, ids=lambda w: w.name)
+def test_modulate_wide(w):
+    _modulate_case(w)
+
+
 @pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
 def test_modulate_full(w):
     _modulate_case(w, sample_rows(w, per_seq=512) if w.tokens > 20000 else None)
