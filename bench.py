@@ -40,6 +40,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup-min-s", type=float, default=0.25,
+                   help="keep running untimed warmup steps (beyond --warmup) until this much wall "
+                        "time has passed: an idle MI355X needs about 40 ms of load to reach its "
+                        "sustained clocks, longer than a few steps of the small workloads")
     p.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_KEYS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -126,10 +130,16 @@ def main():
             launch("attn")
         launch("residual_euler")
 
-    for _ in range(args.warmup):
+    warm_steps = 0
+    t_warm = time.time()
+    while warm_steps < args.warmup or time.time() - t_warm < args.warmup_min_s:
         step(False)
+        warm_steps += 1
+        if warm_steps % 8 == 0:
+            torch.cuda.synchronize()   # the wall clock must see the GPU's progress
     torch.cuda.synchronize()
-    print(f"[bench] {w.name}: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] {w.name}: {warm_steps} warmup steps done, timing {args.steps} steps",
+          file=sys.stderr, flush=True)
 
     # timed region: K whole steps; the attention launches inside it carry their own events
     t0 = torch.cuda.Event(enable_timing=True)
@@ -210,7 +220,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warm_steps,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

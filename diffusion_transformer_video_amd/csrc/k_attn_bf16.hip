@@ -260,13 +260,16 @@ __device__ __forceinline__ float max16(const f32x16& S) {
     return __builtin_fmaxf(mx, S[15]);
 }
 
-// Online-softmax bookkeeping of one tile for one query block: raise the running
-// max (and rescale O and l) only if the tile max exceeds it by more than
-// 2^kLazyRescale.
+// Online-softmax bookkeeping of one tile for one query block: the scaled tile
+// max (tile_max), then raise the running max (and rescale O and l) only if the
+// tile max exceeds it by more than 2^kLazyRescale (raise_max; wave-uniform
+// branch).
+__device__ __forceinline__ float tile_max(const f32x16& S0, const f32x16& S1, float c) {
+    return pair_max(__builtin_fmaxf(max16(S0), max16(S1))) * c;
+}
+
 template <int NDT>
-__device__ __forceinline__ void tile_max_update(const f32x16& S0, const f32x16& S1, f32x16 (&O)[NDT],
-                                                float& m_run, float& l_run, float c) {
-    const float mxs = pair_max(__builtin_fmaxf(max16(S0), max16(S1))) * c;
+__device__ __forceinline__ void raise_max(float mxs, f32x16 (&O)[NDT], float& m_run, float& l_run) {
     if (__builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0) {
         const float m_new = __builtin_fmaxf(m_run, mxs);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -279,19 +282,27 @@ __device__ __forceinline__ void tile_max_update(const f32x16& S0, const f32x16& 
     }
 }
 
-// Probabilities of 8 scores -> one bf16x8 B operand; the row sum accumulates the
-// rounded values (v_dot2 with ones), i.e. exactly the weights of the product.
-__device__ __forceinline__ bf16x8 probs8(const f32x16& S, int t, float c, float m_run, float& l_run) {
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+// Probabilities of 8 scores -> one bf16x8 B operand.
+__device__ __forceinline__ bf16x8 probs8(const f32x16& S, int t, float c, float m_run) {
     uint32_t w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(S[8 * t + 2 * e], c, -m_run));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(S[8 * t + 2 * e + 1], c, -m_run));
         w[e] = pack_bf16x2(p0, p1);
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), ones, l_run, false);
     }
     return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+// Row-sum contribution of one B operand: the rounded bf16 values (v_dot2 with
+// ones), i.e. exactly the weights the product used.
+__device__ __forceinline__ void rowsum8(const bf16x8& P, float& l_run) {
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const uint4 w = __builtin_bit_cast(uint4, P);
+    l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), ones, l_run, false);
+    l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), ones, l_run, false);
+    l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), ones, l_run, false);
+    l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), ones, l_run, false);
 }
 
 // V^T operand for one MFMA step: 4 consecutive keys at byte address a + OFF and 4
@@ -322,6 +333,24 @@ __device__ __forceinline__ void pv_step(const uint32_t (&vb)[Cfg<HD, NW>::NDT], 
     }
 }
 
+template <int HD, int NW, int QB, int KB, int T>
+__device__ __forceinline__ void pv_read(const uint32_t (&vb)[Cfg<HD, NW>::NDT], bf16x8 (&v)[Cfg<HD, NW>::NDT]) {
+    using C = Cfg<HD, NW>;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) v[dt] = vt_operand<(32 * KB + 16 * T) * C::ROWB, 8 * C::ROWB>(vb[dt]);
+}
+
+template <int HD, int NW, int QB>
+__device__ __forceinline__ void pv_mfma(const bf16x8 (&v)[Cfg<HD, NW>::NDT], const bf16x8 (&P)[QB][4], int i,
+                                        f32x16 (&O)[QB][Cfg<HD, NW>::NDT]) {
+    using C = Cfg<HD, NW>;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            O[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[dt], P[qb][i], O[qb][dt], 0, 0, 0);
+}
+
 template <int HD, int NW, int QB>
 __device__ __forceinline__ void pv_tile(uint32_t vread, const int (&vaddr)[Cfg<HD, NW>::NDT],
                                         const bf16x8 (&P)[QB][4], f32x16 (&O)[QB][Cfg<HD, NW>::NDT]) {
@@ -350,27 +379,46 @@ struct Pipe {
     float c;
 };
 
-// Softmax of the tile held in S: running-max update and the bf16 probabilities
-// P[qb][2kb + t] for each query block.
+// Running-max update for the tile held in S (before its probabilities are formed).
 template <int HD, int NW, int QB>
-__device__ __forceinline__ void softmax_tile(Pipe<HD, NW, QB>& p, const f32x16 (&S)[QB][2],
-                                             bf16x8 (&P)[QB][4]) {
+__device__ __forceinline__ void max_update(Pipe<HD, NW, QB>& p, const f32x16 (&S)[QB][2]) {
     using C = Cfg<HD, NW>;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        tile_max_update<C::NDT>(S[qb][0], S[qb][1], p.O[qb], p.m_run[qb], p.l_run[qb], p.c);
+    for (int qb = 0; qb < QB; ++qb)
+        raise_max<C::NDT>(tile_max(S[qb][0], S[qb][1], p.c), p.O[qb], p.m_run[qb], p.l_run[qb]);
+}
+
+// bf16 probabilities P[qb][2kb + t] of the tile held in S (running max already
+// raised for it).
+template <int HD, int NW, int QB>
+__device__ __forceinline__ void probs_tile(const Pipe<HD, NW, QB>& p, const f32x16 (&S)[QB][2],
+                                           bf16x8 (&P)[QB][4]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) P[qb][2 * kb + t] = probs8(S[qb][kb], t, p.c, p.m_run[qb], p.l_run[qb]);
-    }
+            for (int t = 0; t < 2; ++t) P[qb][2 * kb + t] = probs8(S[qb][kb], t, p.c, p.m_run[qb]);
 }
 
-// One pipeline step for tile j (S = S(j) in registers; K(j+1) and V(j) resident):
-// stream K(j+ST) and V(j+ST-1) into their ring slots, softmax of S(j) ||
-// S(j+1) = K(j+1) Q^T, then O += V(j) P(j); finally wait for the tiles the next
-// step needs and publish them with a barrier. Requires j+1 < ntiles.
 template <int HD, int NW, int QB>
+__device__ __forceinline__ void rowsum_tile(Pipe<HD, NW, QB>& p, const bf16x8 (&P)[QB][4]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rowsum8(P[qb][i], p.l_run[qb]);
+}
+
+// One pipeline step for tile j (S = S(j) in registers with the running max
+// already raised for it; K(j+1) and V(j) resident): stream K(j+ST) and V(j+ST-1)
+// into their ring slots; P(j) on the vector ALU while the matrix cores compute
+// S(j+1) = K(j+1) Q^T; O += V(j) P(j) while the vector ALU forms the row sums of
+// P(j) and the max of S(j+1) (masked first when it is the last tile, LAST) -- so
+// the rarely taken rescale branch comes after all of the step's products are
+// issued and never splits them from the softmax work; finally wait for the
+// tiles the next step needs and publish them with a barrier. Requires
+// j+1 < ntiles.
+template <int HD, int NW, int QB, bool LAST>
 __device__ __forceinline__ void pipe_step(Pipe<HD, NW, QB>& p, int j, f32x16 (&S)[QB][2], char* kring,
                                           char* vring) {
     using C = Cfg<HD, NW>;
@@ -390,14 +438,20 @@ __device__ __forceinline__ void pipe_step(Pipe<HD, NW, QB>& p, int j, f32x16 (&S
     if constexpr (QB == 1 && NW == 4) {   // registers to spare: read all K operands first
         bf16x8 ka[2 * C::NKK];
         k_fetch<HD, NW>(kread, p.kaddr, ka);
-        softmax_tile<HD, NW, QB>(p, S, P);
+        probs_tile<HD, NW, QB>(p, S, P);
         s_mfma<HD, NW, QB>(ka, p.qreg, S);   // S(j+1): independent of the exps above
     } else {
-        softmax_tile<HD, NW, QB>(p, S, P);
+        probs_tile<HD, NW, QB>(p, S, P);
         s_tile<HD, NW, QB>(kread, p.kaddr, p.qreg, S);   // S(j+1): independent of the exps above
     }
     pv_tile<HD, NW, QB>(vread, p.vaddr, P, p.O);
-    if (j + 1 == p.ntiles - 1) mask_tile<QB>(S, p.g, (j + 1) * C::BK, p.len);
+    rowsum_tile<HD, NW, QB>(p, P);
+    if constexpr (LAST) mask_tile<QB>(S, p.g, (j + 1) * C::BK, p.len);
+    float mxs[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mxs[qb] = tile_max(S[qb][0], S[qb][1], p.c);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) raise_max<C::NDT>(mxs[qb], p.O[qb], p.m_run[qb], p.l_run[qb]);
     // the next step reads K(j+2) and V(j+1): with a 2-deep ring they were issued in
     // this step, with a 3-deep ring in the previous one, so this step's own loads
     // (completing in issue order) may stay in flight
@@ -415,12 +469,14 @@ __device__ __forceinline__ void pipe_step(Pipe<HD, NW, QB>& p, int j, f32x16 (&S
     __syncthreads();   // everyone's loads have landed; all reads of tile j are done
 }
 
-// Final tile (S = S(j) in registers, V(j) at LDS address vread).
+// Final tile (S = S(j) in registers, running max raised for it; V(j) at LDS
+// address vread).
 template <int HD, int NW, int QB>
 __device__ __forceinline__ void pipe_last(Pipe<HD, NW, QB>& p, const f32x16 (&S)[QB][2], uint32_t vread) {
     bf16x8 P[QB][4];
-    softmax_tile<HD, NW, QB>(p, S, P);
+    probs_tile<HD, NW, QB>(p, S, P);
     pv_tile<HD, NW, QB>(vread, p.vaddr, P, p.O);
+    rowsum_tile<HD, NW, QB>(p, P);
 }
 
 // QB = query blocks of 32 per wave. QB = 2 halves the LDS operand traffic per
@@ -572,6 +628,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
         s_mfma<HD, NW, QB>(ka, p.qreg, S);
     }
     if (p.ntiles == 1) mask_tile<QB>(S, p.g, 0, len);
+    max_update<HD, NW, QB>(p, S);
     // every wave's reads of K(0) are done before step 0 streams into its slot
     __syncthreads();
     if constexpr (C::ST == 3) {
@@ -582,7 +639,8 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     }
 
     // ---- steady state: step j reads K(j+1), V(j) from ring slots (j+1) % ST, j % ST
-    for (int j = 0; j + 1 < p.ntiles; ++j) pipe_step<HD, NW, QB>(p, j, S, kbuf[0], vbuf[0]);
+    for (int j = 0; j + 2 < p.ntiles; ++j) pipe_step<HD, NW, QB, false>(p, j, S, kbuf[0], vbuf[0]);
+    if (p.ntiles > 1) pipe_step<HD, NW, QB, true>(p, p.ntiles - 2, S, kbuf[0], vbuf[0]);
     pipe_last<HD, NW, QB>(p, S, lds_addr(vbuf[0]) + ((p.ntiles - 1) % C::ST) * C::TILEB);
 
     // ---- normalise and store: lane holds query my_q[qb], d = 32dt + 8(r/4) + 4g + r%4
