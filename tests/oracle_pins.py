@@ -35,6 +35,7 @@ def real_impl():
         layer_norm=o_mod.layer_norm, adaln_modulate=o_mod.adaln_modulate,
         apply_rope=o_rope.apply_rope,
         attention=o_attn.attention, attention_bruteforce=o_attn.attention_bruteforce,
+        attention_lse=o_attn.attention_lse, merge=o_attn.merge,
         gated_residual=o_epi.gated_residual, euler_step=o_epi.euler_step,
         interpolant=o_epi.interpolant, velocity=o_epi.velocity,
     )
@@ -308,6 +309,117 @@ def pin_attn_row_subset(impl):
 
 
 # ---------------------------------------------------------------- epilogue
+# ------------------------------------------------- attention LSE and merge
+def pin_lse_zero_query(impl):
+    """q = 0: every score is 0, so lse = ln(number of keys) and o = mean(V)."""
+    _, k, v = _qkv(31, 23)
+    q = np.zeros((5, 2, 16))
+    o, lse = impl.attention_lse(q, k, v, [0, 5], [0, 23])
+    assert np.allclose(lse, math.log(23), rtol=0, atol=1e-12)
+    assert np.allclose(o, np.broadcast_to(v.mean(axis=0), o.shape), atol=1e-12)
+
+
+def pin_lse_single_key(impl):
+    """One key: lse is that key's score q.k / sqrt(d) and o is its value."""
+    q, k, v = _qkv(32, 6)
+    o, lse = impl.attention_lse(q, k[:1], v[:1], [0, 6], [0, 1])
+    ref = np.einsum("nhd,hd->nh", q, k[0]) / 4.0   # sqrt(16)
+    assert np.allclose(lse, ref, rtol=0, atol=1e-12)
+    assert np.allclose(o, np.broadcast_to(v[0], o.shape), atol=1e-12)
+
+
+def pin_lse_identical_keys(impl):
+    """N identical keys: lse = score + ln N."""
+    q, k, v = _qkv(33, 11)
+    k[:] = k[0:1]
+    _, lse = impl.attention_lse(q, k, v, [0, 11], [0, 11])
+    ref = np.einsum("nhd,hd->nh", q, k[0]) / 4.0 + math.log(11)
+    assert np.allclose(lse, ref, rtol=0, atol=1e-12)
+
+
+def pin_lse_library(impl):
+    """lse and o against torch's CPU float64 logsumexp / softmax on the scores,
+    with query and key sets of different sizes and a large score offset."""
+    r = _rng(34)
+    q = r.standard_normal((7, 3, 16)) * 6.0
+    k = r.standard_normal((19, 3, 16)) * 6.0
+    v = r.standard_normal((19, 3, 16))
+    o, lse = impl.attention_lse(q, k, v, [0, 7], [0, 19])
+    S = torch.einsum("qhd,khd->hqk", torch.from_numpy(q), torch.from_numpy(k)) / 4.0
+    ref_lse = torch.logsumexp(S, dim=-1).T.numpy()
+    ref_o = torch.einsum("hqk,khd->qhd", torch.softmax(S, dim=-1), torch.from_numpy(v)).numpy()
+    assert np.allclose(lse, ref_lse, rtol=0, atol=1e-10)
+    assert np.allclose(o, ref_o, rtol=0, atol=1e-12)
+
+
+def pin_lse_empty_keys(impl):
+    """A sequence whose key set is empty: lse = -inf, o = 0; others unaffected."""
+    q, k, v = _qkv(35, 9)
+    o, lse = impl.attention_lse(q, k, v, [0, 4, 9], [0, 0, 9])
+    assert np.all(np.isneginf(lse[:4])) and np.all(o[:4] == 0.0)
+    o2, lse2 = impl.attention_lse(q[4:], k, v, [0, 5], [0, 9])
+    assert np.allclose(o[4:], o2, atol=1e-14) and np.allclose(lse[4:], lse2, atol=1e-14)
+
+
+def pin_lse_matches_softmax_attention(impl):
+    """With each sequence's queries and keys the same token set, o is the
+    attention of the block (and lse is finite)."""
+    q, k, v = _qkv(36, 30)
+    cu = [0, 12, 30]
+    o, lse = impl.attention_lse(q, k, v, cu, cu)
+    assert np.allclose(o, impl.attention(q, k, v, cu), atol=1e-12)
+    assert np.all(np.isfinite(lse))
+
+
+def pin_merge_split_equals_full(impl):
+    """Attention over a key set equals the merge of the attentions over any
+    split of it into two disjoint parts (the ring / context-parallel identity),
+    for several sequences with different split points."""
+    r = _rng(37)
+    q = r.standard_normal((10, 2, 16)) * 2.0
+    k = r.standard_normal((15, 2, 16)) * 2.0
+    v = r.standard_normal((15, 2, 16))
+    cq, ck = [0, 4, 10], [0, 7, 15]
+    o, lse = impl.attention_lse(q, k, v, cq, ck)
+    i1, i2 = np.r_[0:2, 7:13], np.r_[2:7, 13:15]
+    o1, l1 = impl.attention_lse(q, k[i1], v[i1], cq, [0, 2, 8])
+    o2, l2 = impl.attention_lse(q, k[i2], v[i2], cq, [0, 5, 7])
+    om, lm = impl.merge(o1, l1, o2, l2)
+    assert np.allclose(om, o, rtol=0, atol=1e-12) and np.allclose(lm, lse, rtol=0, atol=1e-12)
+    om, lm = impl.merge(o2, l2, o1, l1)   # order does not matter
+    assert np.allclose(om, o, rtol=0, atol=1e-12) and np.allclose(lm, lse, rtol=0, atol=1e-12)
+
+
+def pin_merge_empty_identity(impl):
+    """Merging with an empty partial (lse = -inf) leaves a partial unchanged;
+    two empty partials stay empty (o = 0, lse = -inf)."""
+    r = _rng(38)
+    o = r.standard_normal((6, 2, 16))
+    lse = r.standard_normal((6, 2)) * 3.0
+    zo, zl = np.zeros_like(o), np.full_like(lse, -np.inf)
+    om, lm = impl.merge(o, lse, zo, zl)
+    assert np.allclose(om, o, atol=1e-15) and np.array_equal(lm, lse)
+    om, lm = impl.merge(zo, zl, zo, zl)
+    assert np.all(om == 0.0) and np.all(np.isneginf(lm))
+
+
+def pin_merge_weights_bruteforce(impl):
+    """Merge against a per-element loop that re-weights each partial by its share
+    of the joint exponential sum, computed as exp(l_a) / (exp(l_a) + exp(l_b))
+    on moderate values (no overflow)."""
+    r = _rng(39)
+    oa, ob = r.standard_normal((3, 2, 4)), r.standard_normal((3, 2, 4))
+    la, lb = r.standard_normal((3, 2)), r.standard_normal((3, 2))
+    om, lm = impl.merge(oa, la, ob, lb)
+    for i in range(3):
+        for h in range(2):
+            ea, eb = math.exp(la[i, h]), math.exp(lb[i, h])
+            assert abs(lm[i, h] - math.log(ea + eb)) < 1e-13
+            for d in range(4):
+                ref = (ea * oa[i, h, d] + eb * ob[i, h, d]) / (ea + eb)
+                assert abs(om[i, h, d] - ref) < 1e-13
+
+
 def pin_residual_alpha0(impl):
     r = _rng(22)
     x = r.standard_normal((6, 32))

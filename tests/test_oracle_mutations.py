@@ -77,6 +77,43 @@ def _attn_with(scale_pow=0.5, use_k_as_v=False, ignore_cu=False, transpose_score
     return f
 
 
+def _lse_with(log2=False, no_scale=False, lse_of_max=False):
+    def f(q, k, v, cu_q, cu_k, num_seqs=1, rows=None, row_block=1024):
+        o, lse = o_attn.attention_lse(q, k, v, cu_q, cu_k, num_seqs, rows, row_block)
+        if log2:
+            lse = lse / math.log(2.0)
+        if lse_of_max:   # drops the log-sum term: returns the row max only
+            cq, ck = list(cu_q), list(cu_k)
+            out = np.full_like(lse, -np.inf)
+            for s in range(len(cq) - 1):
+                if ck[s + 1] > ck[s]:
+                    S = np.einsum("qhd,khd->qhk", q[cq[s]:cq[s + 1]], k[ck[s]:ck[s + 1]]) / math.sqrt(q.shape[-1])
+                    out[cq[s]:cq[s + 1]] = S.max(axis=-1)
+            lse = out
+        if no_scale:
+            lse = lse * math.sqrt(q.shape[-1])
+        return o, lse
+    return f
+
+
+def _merge_with(swap_weights=False, no_renorm=False):
+    def f(o_a, lse_a, o_b, lse_b):
+        o, lse = o_attn.merge(o_a, lse_a, o_b, lse_b)
+        if swap_weights or no_renorm:
+            la, lb = np.asarray(lse_a), np.asarray(lse_b)
+            live = np.isfinite(lse)
+            ref = np.where(live, lse, 0.0)
+            wa = np.where(live, np.exp(la - ref), 0.0)
+            wb = np.where(live, np.exp(lb - ref), 0.0)
+            if swap_weights:
+                wa, wb = wb, wa
+            if no_renorm:
+                wa, wb = np.ones_like(wa), np.ones_like(wb)
+            o = wa[..., None] * o_a + wb[..., None] * o_b
+        return o, lse
+    return f
+
+
 def _coords_swapped(n, gh, gw):
     n = np.asarray(n, dtype=np.int64)
     return np.stack([n // (gh * gw), n % gw, (n // gw) % gh], axis=-1)
@@ -120,6 +157,11 @@ MUTANTS = {
     "attn_k_as_v": dict(attention=_attn_with(use_k_as_v=True)),
     "attn_across_sequences": dict(attention=_attn_with(ignore_cu=True)),
     "attn_transposed_scores": dict(attention=_attn_with(transpose_scores=True)),
+    "lse_base2": dict(attention_lse=_lse_with(log2=True)),
+    "lse_unscaled": dict(attention_lse=_lse_with(no_scale=True)),
+    "lse_max_only": dict(attention_lse=_lse_with(lse_of_max=True)),
+    "merge_swapped_weights": dict(merge=_merge_with(swap_weights=True)),
+    "merge_no_renormalise": dict(merge=_merge_with(no_renorm=True)),
     "grid_h_w_swapped": dict(coords=_coords_swapped),
     "interpolant_reversed": dict(interpolant=_interp_reversed),
     "euler_wrong_sign": dict(euler_step=_euler_minus),
