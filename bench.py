@@ -198,17 +198,48 @@ def main():
         for i in range(R)])
     del xs, os_, xo, zs, us, zo
 
+    # ring-attention building blocks (not part of the step): attention with the row
+    # log-sum-exp (keys = the queries' own tokens, so its flops equal attn's), and
+    # the fold of a bf16 partial into a float32 accumulator
+    lse = torch.empty(w.tokens, w.heads, dtype=torch.float32, device="cuda")
+
+    def attn_lse():
+        if cu is None:
+            dit.dit_attn3d_lse(o, lse, q, k, v, num_seqs=w.num_seqs)
+        else:
+            dit.dit_attn3d_lse(o, lse, q, k, v, cu, cu, max_seqlen_q=w.max_seqlen, max_seqlen_k=w.max_seqlen)
+    attn_lse()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        attn_lse()
+    e1.record()
+    torch.cuda.synchronize()
+    kern_ms["attn_lse"] = e0.elapsed_time(e1) / 3
+    merge_bytes = w.tokens * w.d_model * (4 + 4 + esz) + w.tokens * w.heads * (4 + 4 + 4)
+    R = rotation(merge_bytes)
+    accs = [torch.zeros(w.tokens, w.heads, w.head_dim, dtype=torch.float32, device="cuda") for _ in range(R)]
+    laccs = [lse.clone() for _ in range(R)]
+    obs = [o.clone() for _ in range(R)]
+    lbs = [lse.clone() for _ in range(R)]
+    kern_ms["merge"] = timed_batch([(lambda i=i: dit.dit_attn_merge(accs[i], laccs[i], obs[i], lbs[i]))
+                                    for i in range(R)])
+    del accs, laccs, obs, lbs
+
     flops = w.attn_flops()
     tok, D, P = w.tokens, w.d_model, synth.LATENT_CHANNELS
     algo_bytes = {
         "modulate": 2 * tok * D * esz,
         "rope": 4 * tok * D * esz,
         "residual_euler": 3 * tok * D * esz + 3 * tok * P * esz,
+        "merge": merge_bytes,
     }
     attn_s = kern_ms["attn"] * 1e-3
     achieved = flops / attn_s / 1e12
     traffic = traffic_for(w.name)
-    kernels = {"attn": {"us": round(kern_ms["attn"] * 1e3, 2), "tflops": round(achieved, 2)}}
+    kernels = {"attn": {"us": round(kern_ms["attn"] * 1e3, 2), "tflops": round(achieved, 2)},
+               "attn_lse": {"us": round(kern_ms["attn_lse"] * 1e3, 2),
+                            "tflops": round(flops / (kern_ms["attn_lse"] * 1e-3) / 1e12, 2)}}
     for n, nb in algo_bytes.items():
         gbs = nb / (kern_ms[n] * 1e-3) / 1e9
         kernels[n] = {"us": round(kern_ms[n] * 1e3, 2), "gbs": round(gbs, 1),
@@ -233,7 +264,7 @@ def main():
                    "rope_split": list(w.rope_split), "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_bf16_kernel<128,4>",
+                     "traffic": traffic, "kernel": "attn_bf16_kernel<128,8,1>",
                      "flops_per_launch": flops},
         "kernels": kernels,
     }

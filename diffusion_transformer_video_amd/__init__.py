@@ -27,7 +27,7 @@ DIT_F32, DIT_BF16 = 0, 1
 DIT_OK, DIT_E_INVAL, DIT_E_UNSUPPORTED, DIT_E_HIP = 0, 1, 2, 3
 
 EXPORTS = ("dit_last_error", "dit_version", "dit_adaln_modulate", "dit_rope3d",
-           "dit_attn3d", "dit_gated_residual", "rf_euler_step")
+           "dit_attn3d", "dit_attn3d_lse", "dit_attn_merge", "dit_gated_residual", "rf_euler_step")
 
 
 class DitError(RuntimeError):
@@ -65,6 +65,10 @@ def lib() -> ctypes.CDLL:
                                  i32, i32, i32, f32, vp, i32, vp]
         L.dit_attn3d.restype = ctypes.c_int
         L.dit_attn3d.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, vp]
+        L.dit_attn3d_lse.restype = ctypes.c_int
+        L.dit_attn3d_lse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, vp, vp, i32, i32, i32, i32, vp]
+        L.dit_attn_merge.restype = ctypes.c_int
+        L.dit_attn_merge.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, vp]
         L.dit_gated_residual.restype = ctypes.c_int
         L.dit_gated_residual.argtypes = [vp, vp, vp, vp, i64, i32, i64,
                                          ctypes.POINTER(EulerArgs), i32, vp]
@@ -107,7 +111,7 @@ def _f32(*ts) -> None:
     torch = _torch()
     for t in ts:
         if t.dtype != torch.float32:
-            raise TypeError("parameter tables (gamma, beta, alpha, dt_rows) must be float32")
+            raise TypeError("parameter tables (gamma, beta, alpha, dt_rows) and lse / accumulators must be float32")
 
 
 def _stream(stream) -> int:
@@ -163,6 +167,46 @@ def dit_attn3d(o, q, k, v, cu_seqlens=None, num_seqs: int = 1, max_seqlen: int =
                             _ptr(cu_seqlens), int(num_seqs), int(max_seqlen), _dtype_code(q),
                             _stream(stream)))
     return o
+
+
+def dit_attn3d_lse(o, lse, q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, num_seqs: int = 1,
+                   max_seqlen_q: int = 0, max_seqlen_k: int = 0, stream=None):
+    """One ring step: o, lse of each sequence's queries against its own key block.
+
+    q, o [tokens_q, heads, hd]; k, v [tokens_k, heads, hd]; lse [tokens_q, heads]
+    float32 (natural log). cu_seqlens_q / cu_seqlens_k: both None (dense,
+    num_seqs equal sequences) or both device int32 [num_seqs + 1]."""
+    _dev(o, lse, q, k, v, cu_seqlens_q, cu_seqlens_k)
+    _f32(lse)
+    if q.dim() != 3 or o.shape != q.shape or any(t.dtype != q.dtype for t in (k, v, o)):
+        raise ValueError("o, q must be [tokens_q, heads, head_dim] and k, v share their dtype")
+    if k.dim() != 3 or v.shape != k.shape or k.shape[1:] != q.shape[1:]:
+        raise ValueError("k, v must be [tokens_k, heads, head_dim] with the heads and head_dim of q")
+    if lse.shape != q.shape[:2]:
+        raise ValueError("lse must be [tokens_q, heads]")
+    tq, heads, hd = q.shape
+    if cu_seqlens_q is not None:
+        num_seqs = cu_seqlens_q.numel() - 1
+        if cu_seqlens_k is None or cu_seqlens_k.numel() != num_seqs + 1:
+            raise ValueError("cu_seqlens_k must have as many sequences as cu_seqlens_q")
+    _check(lib().dit_attn3d_lse(_ptr(o), _ptr(lse), _ptr(q), _ptr(k), _ptr(v), tq, k.shape[0], heads, hd,
+                                _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(num_seqs), int(max_seqlen_q),
+                                int(max_seqlen_k), _dtype_code(q), _stream(stream)))
+    return o, lse
+
+
+def dit_attn_merge(o_acc, lse_acc, o_b, lse_b, stream=None):
+    """(o_acc, lse_acc) <- merge with the partial (o_b, lse_b), in place.
+    o_acc float32 [tokens, heads, hd]; o_b [tokens, heads, hd] (bf16 or float32);
+    lse_acc, lse_b float32 [tokens, heads]."""
+    _dev(o_acc, lse_acc, o_b, lse_b)
+    _f32(o_acc, lse_acc, lse_b)
+    if o_acc.dim() != 3 or o_b.shape != o_acc.shape or lse_acc.shape != o_acc.shape[:2] or lse_b.shape != lse_acc.shape:
+        raise ValueError("o_acc, o_b must be [tokens, heads, head_dim] and lse_acc, lse_b [tokens, heads]")
+    tokens, heads, hd = o_acc.shape
+    _check(lib().dit_attn_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_b), _ptr(lse_b), tokens, heads, hd,
+                                _dtype_code(o_b), _stream(stream)))
+    return o_acc, lse_acc
 
 
 def dit_gated_residual(x_out, x, branch, alpha, tokens_per_row: int, euler=None, stream=None):

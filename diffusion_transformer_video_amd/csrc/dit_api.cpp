@@ -168,44 +168,103 @@ int dit_rope3d(void* q, void* k, int64_t tokens, int32_t heads, int32_t head_dim
     return launched(dit::launch_rope3d(a, dtype == DIT_BF16, (hipStream_t)stream), fn);
 }
 
-int dit_attn3d(void* o, const void* q, const void* k, const void* v,
-               int64_t tokens, int32_t heads, int32_t head_dim,
-               const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
-               int32_t dtype, void* stream) {
-    const char* fn = "dit_attn3d";
+namespace {
+
+// Shared validation and launch of dit_attn3d / dit_attn3d_lse.
+int attn_common(const char* fn, void* o, float* lse, const void* q, const void* k, const void* v,
+                int64_t tokens_q, int64_t tokens_k, int32_t heads, int32_t head_dim,
+                const int32_t* cu_q, const int32_t* cu_k, int32_t num_seqs,
+                int32_t max_q, int32_t max_k, int32_t dtype, void* stream) {
     if (int rc = check_dtype(dtype, fn)) return rc;
     if (!o || !q || !k || !v) return fail(DIT_E_INVAL, "%s: NULL pointer argument", fn);
-    if (tokens <= 0) return fail(DIT_E_INVAL, "%s: tokens must be > 0", fn);
+    if (tokens_q <= 0 || tokens_k <= 0) return fail(DIT_E_INVAL, "%s: token counts must be > 0", fn);
     if (heads <= 0) return fail(DIT_E_INVAL, "%s: heads must be > 0", fn);
     if (num_seqs <= 0) return fail(DIT_E_INVAL, "%s: num_seqs must be > 0", fn);
-    int32_t seqlen = max_seqlen;
-    if (cu_seqlens == nullptr) {
-        if (tokens % num_seqs != 0)
-            return fail(DIT_E_INVAL, "%s: dense tokens (%lld) must be a multiple of num_seqs (%d)",
-                        fn, (long long)tokens, num_seqs);
-        if (tokens / num_seqs > 0x7fffffff) return fail(DIT_E_UNSUPPORTED, "%s: sequence too long", fn);
-        seqlen = (int32_t)(tokens / num_seqs);
-    } else if (max_seqlen <= 0 || max_seqlen > tokens) {
-        return fail(DIT_E_INVAL, "%s: packed mode needs 0 < max_seqlen <= tokens (got %d)", fn, max_seqlen);
+    if ((cu_q == nullptr) != (cu_k == nullptr))
+        return fail(DIT_E_INVAL, "%s: query and key offsets must both be given or both be NULL", fn);
+    int32_t seq_q = max_q, seq_k = max_k;
+    if (cu_q == nullptr) {
+        if (tokens_q % num_seqs != 0 || tokens_k % num_seqs != 0)
+            return fail(DIT_E_INVAL, "%s: dense token counts (%lld, %lld) must be multiples of num_seqs (%d)",
+                        fn, (long long)tokens_q, (long long)tokens_k, num_seqs);
+        if (tokens_q / num_seqs > 0x7fffffff || tokens_k / num_seqs > 0x7fffffff)
+            return fail(DIT_E_UNSUPPORTED, "%s: sequence too long", fn);
+        seq_q = (int32_t)(tokens_q / num_seqs);
+        seq_k = (int32_t)(tokens_k / num_seqs);
+    } else {
+        if (max_q <= 0 || max_q > tokens_q)
+            return fail(DIT_E_INVAL, "%s: packed mode needs 0 < max_seqlen <= tokens (got %d)", fn, max_q);
+        if (max_k < 0 || max_k > tokens_k)
+            return fail(DIT_E_INVAL, "%s: packed mode needs 0 <= max key count <= key tokens (got %d)", fn, max_k);
     }
     if (head_dim != 64 && head_dim != 128)
         return fail(DIT_E_UNSUPPORTED, "%s: head_dim must be 64 or 128 (got %d)", fn, head_dim);
     if (!aligned16(o) || !aligned16(q) || !aligned16(k) || !aligned16(v))
         return fail(DIT_E_UNSUPPORTED, "%s: tensors must be 16-byte aligned", fn);
+    if (lse != nullptr && ((uintptr_t)lse % 4) != 0)
+        return fail(DIT_E_UNSUPPORTED, "%s: lse must be 4-byte aligned", fn);
     // the bf16 kernel addresses one sequence of one head with 32-bit byte offsets
-    if ((int64_t)seqlen * heads * head_dim * elem_size(dtype) > INT32_MAX)
+    const int64_t row_bytes = (int64_t)heads * head_dim * elem_size(dtype);
+    if ((int64_t)seq_q * row_bytes > INT32_MAX || (int64_t)seq_k * row_bytes > INT32_MAX)
         return fail(DIT_E_UNSUPPORTED, "%s: sequence length x heads x head_dim too large (%lld bytes per sequence)",
-                    fn, (long long)seqlen * heads * head_dim * elem_size(dtype));
-    const int64_t bytes = tokens * heads * head_dim * elem_size(dtype);
-    if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
+                    fn, (long long)(seq_q > seq_k ? seq_q : seq_k) * row_bytes);
+    const int64_t qbytes = tokens_q * row_bytes, kbytes = tokens_k * row_bytes;
+    if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kbytes) || overlaps(o, qbytes, v, kbytes))
         return fail(DIT_E_INVAL, "%s: o must not overlap q, k or v", fn);
+    if (lse != nullptr) {
+        const int64_t lbytes = tokens_q * heads * 4;
+        if (overlaps(lse, lbytes, o, qbytes) || overlaps(lse, lbytes, q, qbytes) ||
+            overlaps(lse, lbytes, k, kbytes) || overlaps(lse, lbytes, v, kbytes))
+            return fail(DIT_E_INVAL, "%s: lse must not overlap o, q, k or v", fn);
+    }
     if (int rc = check_device(fn)) return rc;
-    dit::AttnArgs a{o, q, k, v, tokens, heads, head_dim, cu_seqlens, num_seqs, seqlen,
+    dit::AttnArgs a{o, q, k, v, tokens_q, heads, head_dim, cu_q, num_seqs, seq_q,
                     (float)(1.4426950408889634 / std::sqrt((double)head_dim)),
-                    (float)(1.0 / std::sqrt((double)head_dim))};
+                    (float)(1.0 / std::sqrt((double)head_dim)), cu_k, seq_k, lse};
     hipError_t e = dtype == DIT_BF16 ? dit::launch_attn3d_bf16(a, (hipStream_t)stream)
                                      : dit::launch_attn3d_f32(a, (hipStream_t)stream);
     return launched(e, fn);
+}
+
+}  // namespace
+
+int dit_attn3d(void* o, const void* q, const void* k, const void* v,
+               int64_t tokens, int32_t heads, int32_t head_dim,
+               const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+               int32_t dtype, void* stream) {
+    return attn_common("dit_attn3d", o, nullptr, q, k, v, tokens, tokens, heads, head_dim, cu_seqlens,
+                       cu_seqlens, num_seqs, max_seqlen, max_seqlen, dtype, stream);
+}
+
+int dit_attn3d_lse(void* o, float* lse, const void* q, const void* k, const void* v,
+                   int64_t tokens_q, int64_t tokens_k, int32_t heads, int32_t head_dim,
+                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                   int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t dtype, void* stream) {
+    if (!lse) return fail(DIT_E_INVAL, "dit_attn3d_lse: NULL pointer argument");
+    return attn_common("dit_attn3d_lse", o, lse, q, k, v, tokens_q, tokens_k, heads, head_dim, cu_seqlens_q,
+                       cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k, dtype, stream);
+}
+
+int dit_attn_merge(float* o_acc, float* lse_acc, const void* o_b, const float* lse_b,
+                   int64_t tokens, int32_t heads, int32_t head_dim, int32_t dtype, void* stream) {
+    const char* fn = "dit_attn_merge";
+    if (int rc = check_dtype(dtype, fn)) return rc;
+    if (!o_acc || !lse_acc || !o_b || !lse_b) return fail(DIT_E_INVAL, "%s: NULL pointer argument", fn);
+    if (tokens <= 0) return fail(DIT_E_INVAL, "%s: tokens must be > 0", fn);
+    if (heads <= 0) return fail(DIT_E_INVAL, "%s: heads must be > 0", fn);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(DIT_E_UNSUPPORTED, "%s: head_dim must be 64 or 128 (got %d)", fn, head_dim);
+    if (!aligned16(o_acc) || !aligned16(o_b) || ((uintptr_t)lse_acc % 4) != 0 || ((uintptr_t)lse_b % 4) != 0)
+        return fail(DIT_E_UNSUPPORTED, "%s: o arrays must be 16-byte and lse arrays 4-byte aligned", fn);
+    const int64_t rows = tokens * heads;
+    const int64_t abytes = rows * head_dim * 4, bbytes = rows * head_dim * elem_size(dtype), lbytes = rows * 4;
+    if (overlaps(o_acc, abytes, o_b, bbytes) || overlaps(o_acc, abytes, lse_acc, lbytes) ||
+        overlaps(o_acc, abytes, lse_b, lbytes) || overlaps(lse_acc, lbytes, o_b, bbytes) ||
+        overlaps(lse_acc, lbytes, lse_b, lbytes) || overlaps(o_b, bbytes, lse_b, lbytes))
+        return fail(DIT_E_INVAL, "%s: the four arrays must not overlap", fn);
+    if (int rc = check_device(fn)) return rc;
+    dit::MergeArgs a{o_acc, lse_acc, o_b, lse_b, rows, head_dim};
+    return launched(dit::launch_attn_merge(a, dtype == DIT_BF16, (hipStream_t)stream), fn);
 }
 
 int dit_gated_residual(void* x_out, const void* x, const void* branch, const float* alpha,

@@ -25,14 +25,27 @@ hipError_t launch_rope3d(const RopeArgs& a, bool bf16, hipStream_t s);
 
 struct AttnArgs {
     void* o; const void* q; const void* k; const void* v;
-    int64_t tokens; int heads; int head_dim;
-    const int32_t* cu_seqlens;   // NULL => dense
+    int64_t tokens; int heads; int head_dim;   // tokens: query rows (q, o)
+    const int32_t* cu_seqlens;   // query offsets; NULL => dense
     int num_seqs; int max_seqlen;   // dense: max_seqlen = tokens / num_seqs
     float scale_log2;            // log2(e) / sqrt(head_dim)
     float scale;                 // 1 / sqrt(head_dim)
+    // keys / values of sequence s: rows cu_seqlens_k[s] .. cu_seqlens_k[s+1] of k, v
+    // (dense: max_seqlen_k rows per sequence). For self-attention these are the
+    // query-side values.
+    const int32_t* cu_seqlens_k; int max_seqlen_k;
+    float* lse;                  // NULL, or [tokens, heads]: ln sum_keys exp(q.k / sqrt(d))
 };
 hipError_t launch_attn3d_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn3d_f32(const AttnArgs& a, hipStream_t s);
+
+// (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_b, lse_b)); o_acc fp32.
+struct MergeArgs {
+    float* o_acc; float* lse_acc; const void* o_b; const float* lse_b;
+    int64_t rows;   // tokens * heads
+    int head_dim;
+};
+hipError_t launch_attn_merge(const MergeArgs& a, bool bf16, hipStream_t s);
 
 struct EulerArgs {
     void* z_out; const void* z; const void* u; const float* dt_rows;

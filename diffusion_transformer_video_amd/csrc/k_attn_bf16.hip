@@ -369,7 +369,7 @@ template <int HD, int NW, int QB>
 struct Pipe {
     using C = Cfg<HD, NW>;
     i32x4 rk, rv;
-    int wave, lane, g, len, ntiles;
+    int wave, lane, g, len, qlen, ntiles;   // len: keys of the sequence; qlen: its queries
     uint32_t ldb, koff, voff;
     int kaddr[C::NKK];
     int vaddr[C::NDT];
@@ -497,8 +497,8 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     // Blocks past the real total (the grid is sized for num_seqs x the longest
     // sequence) are dealt last by the dispatcher and exit at once.
     int total, seq, qt, head;
-    int64_t s0;
-    int len;
+    int64_t s0, k0;   // first query row / first key row of the sequence
+    int len, klen;    // its queries / keys
     if (a.cu_seqlens == nullptr) {
         total = (int)gridDim.x;
     } else {
@@ -523,12 +523,14 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
             qt = __builtin_amdgcn_readfirstlane(r - seq * nqt);
             s0 = (int64_t)seq * a.max_seqlen;
             len = a.max_seqlen;
+            k0 = (int64_t)seq * a.max_seqlen_k;
+            klen = a.max_seqlen_k;
         } else {
             const int per_head = total / a.heads;
             head = __builtin_amdgcn_readfirstlane(w / per_head);
             int r = __builtin_amdgcn_readfirstlane(w - head * per_head);
-            // walk the sequences longest first (ties: lower index first); num_seqs is
-            // small, so the O(n^2) rank walk is a handful of scalar steps
+            // walk the sequences longest first (by queries; ties: lower index first);
+            // num_seqs is small, so the O(n^2) rank walk is a handful of scalar steps
             seq = -1;
             int prev_len = 0x7fffffff, prev_idx = -1;
             for (int k = 0; k < a.num_seqs && seq < 0; ++k) {
@@ -549,10 +551,27 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
             const int c1 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq + 1]);
             s0 = c0;
             len = c1 - c0;
+            const int d0 = __builtin_amdgcn_readfirstlane(a.cu_seqlens_k[seq]);
+            const int d1 = __builtin_amdgcn_readfirstlane(a.cu_seqlens_k[seq + 1]);
+            k0 = d0;
+            klen = d1 - d0;
         }
     }
     const int q0 = qt * BQ;
     if (q0 >= len) return;
+    if (klen == 0) {   // no keys: o = 0, lse = -inf (the empty sum)
+        const int tid = threadIdx.x;
+        for (int i = tid; i < BQ; i += 64 * NW) {
+            const int qi = q0 + i;
+            if (qi >= len) break;
+            const int64_t row = (s0 + qi) * a.heads + head;
+            uint4* Og = reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(a.o) + row * HD);
+#pragma unroll
+            for (int c = 0; c < HD / 8; ++c) Og[c] = make_uint4(0, 0, 0, 0);
+            if (a.lse != nullptr) a.lse[row] = -INFINITY;
+        }
+        return;
+    }
 
     Pipe<HD, NW, QB> p;
     const int tid = threadIdx.x;
@@ -560,15 +579,18 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     p.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     p.g = p.lane >> 5;
     const int l32 = p.lane & 31;
-    p.len = len;
-    p.ntiles = (len + C::BK - 1) / C::BK;
+    p.len = klen;
+    p.qlen = len;
+    p.ntiles = (klen + C::BK - 1) / C::BK;
     p.ldb = (uint32_t)a.heads * HD * 2;   // token stride in bytes
     const int64_t base = (s0 * a.heads + head) * (int64_t)HD;   // element offset of (s0, head, 0)
-    const uint32_t span = (uint32_t)len * p.ldb;   // bytes of this sequence (< 2^31, host-checked)
+    const int64_t kbase = (k0 * a.heads + head) * (int64_t)HD;  // element offset of (k0, head, 0)
+    // bytes of this sequence's queries / keys (< 2^31, host-checked)
+    const uint32_t qspan = (uint32_t)len * p.ldb, kspan = (uint32_t)klen * p.ldb;
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(reinterpret_cast<const __bf16*>(a.q) + base), (short)0, span, 0x00020000);
-    p.rk = make_rsrc(reinterpret_cast<const __bf16*>(a.k) + base, span);
-    p.rv = make_rsrc(reinterpret_cast<const __bf16*>(a.v) + base, span);
+        (void*)(reinterpret_cast<const __bf16*>(a.q) + base), (short)0, qspan, 0x00020000);
+    p.rk = make_rsrc(reinterpret_cast<const __bf16*>(a.k) + kbase, kspan);
+    p.rv = make_rsrc(reinterpret_cast<const __bf16*>(a.v) + kbase, kspan);
 
     // ---- per-lane, loop-invariant offsets
     {
@@ -615,10 +637,10 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
 
     // ---- prologue: K(0), V(0), K(1) resident; S(0); then the loads a step -1
     // would have issued (K(ST-1), V(ST-2)) for a 3-deep ring
-    issue_any<HD, NW, false>(p.rk, kbuf[0], p.wave, p.lane, p.ldb, 0, (uint32_t)len, p.koff);
-    issue_any<HD, NW, true>(p.rv, vbuf[0], p.wave, p.lane, p.ldb, 0, (uint32_t)len, p.voff);
+    issue_any<HD, NW, false>(p.rk, kbuf[0], p.wave, p.lane, p.ldb, 0, (uint32_t)klen, p.koff);
+    issue_any<HD, NW, true>(p.rv, vbuf[0], p.wave, p.lane, p.ldb, 0, (uint32_t)klen, p.voff);
     if (p.ntiles > 1)
-        issue_any<HD, NW, false>(p.rk, kbuf[1], p.wave, p.lane, p.ldb, C::BK, (uint32_t)len, p.koff);
+        issue_any<HD, NW, false>(p.rk, kbuf[1], p.wave, p.lane, p.ldb, C::BK, (uint32_t)klen, p.koff);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     f32x16 S[QB][2];
@@ -627,15 +649,15 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
         k_fetch<HD, NW>(lds_addr(kbuf[0]), p.kaddr, ka);
         s_mfma<HD, NW, QB>(ka, p.qreg, S);
     }
-    if (p.ntiles == 1) mask_tile<QB>(S, p.g, 0, len);
+    if (p.ntiles == 1) mask_tile<QB>(S, p.g, 0, klen);
     max_update<HD, NW, QB>(p, S);
     // every wave's reads of K(0) are done before step 0 streams into its slot
     __syncthreads();
     if constexpr (C::ST == 3) {
         if (p.ntiles > 2)
-            issue_any<HD, NW, false>(p.rk, kbuf[2], p.wave, p.lane, p.ldb, 2 * C::BK, (uint32_t)len, p.koff);
+            issue_any<HD, NW, false>(p.rk, kbuf[2], p.wave, p.lane, p.ldb, 2 * C::BK, (uint32_t)klen, p.koff);
         if (p.ntiles > 1)
-            issue_any<HD, NW, true>(p.rv, vbuf[1], p.wave, p.lane, p.ldb, C::BK, (uint32_t)len, p.voff);
+            issue_any<HD, NW, true>(p.rv, vbuf[1], p.wave, p.lane, p.ldb, C::BK, (uint32_t)klen, p.voff);
     }
 
     // ---- steady state: step j reads K(j+1), V(j) from ring slots (j+1) % ST, j % ST
@@ -643,13 +665,15 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     if (p.ntiles > 1) pipe_step<HD, NW, QB, true>(p, p.ntiles - 2, S, kbuf[0], vbuf[0]);
     pipe_last<HD, NW, QB>(p, S, lds_addr(vbuf[0]) + ((p.ntiles - 1) % C::ST) * C::TILEB);
 
-    // ---- normalise and store: lane holds query my_q[qb], d = 32dt + 8(r/4) + 4g + r%4
+    // ---- normalise and store: lane holds query my_q[qb], d = 32dt + 8(r/4) + 4g + r%4;
+    // lanes l and l^32 summed disjoint keys of the same query
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const float inv = 1.0f / pair_sum(p.l_run[qb]);   // lanes l and l^32 summed disjoint keys
+        const float l = pair_sum(p.l_run[qb]);
+        const float inv = 1.0f / l;
         if (my_q[qb] < len) {
-            uint2* Og = reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(a.o) + base +
-                                                 (int64_t)my_q[qb] * a.heads * HD);
+            const int64_t row = (s0 + my_q[qb]) * a.heads + head;
+            uint2* Og = reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(a.o) + row * HD);
 #pragma unroll
             for (int dt = 0; dt < C::NDT; ++dt) {
 #pragma unroll
@@ -660,6 +684,9 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
                     Og[(dt * 32 + 8 * rg + 4 * p.g) / 4] = wv;
                 }
             }
+            // ln sum_keys exp(s) = ln 2 * (m + log2 l): scores were exponentiated as
+            // exp2(s * log2(e) - m)
+            if (a.lse != nullptr && p.g == 0) a.lse[row] = (p.m_run[qb] + __log2f(l)) * 0.69314718055994531f;
         }
     }
 }

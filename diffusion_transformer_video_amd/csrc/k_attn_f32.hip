@@ -9,7 +9,9 @@
 // fp32 so results stay within 1e-4 of the exact softmax: one thread owns one
 // query row (q and the output accumulator in registers), key/value tiles are
 // staged through LDS and read as broadcasts, and the softmax is evaluated
-// online per key tile with exact expf.
+// online per key tile with exact expf. Queries and keys may come from separate
+// packed sets (a sequence's keys in their own block); the row log-sum-exp of the
+// scaled scores is m + ln l.
 #include <math.h>
 
 #include "dit_device.hpp"
@@ -27,23 +29,27 @@ __global__ __launch_bounds__(kQ) void attn_f32_kernel(AttnArgs a) {
     __shared__ float vs[kK][HD];
     const int head = blockIdx.y;
     const int seq = blockIdx.z;
-    int64_t s0, s1;
+    int64_t s0, s1, k0, k1;   // query rows / key rows of the sequence
     if (a.cu_seqlens == nullptr) {
         s0 = (int64_t)seq * a.max_seqlen;
         s1 = s0 + a.max_seqlen;
+        k0 = (int64_t)seq * a.max_seqlen_k;
+        k1 = k0 + a.max_seqlen_k;
     } else {
         s0 = a.cu_seqlens[seq];
         s1 = a.cu_seqlens[seq + 1];
+        k0 = a.cu_seqlens_k[seq];
+        k1 = a.cu_seqlens_k[seq + 1];
     }
-    const int64_t len = s1 - s0;
+    const int64_t len = s1 - s0, klen = k1 - k0;
     const int64_t q0 = (int64_t)blockIdx.x * kQ;
     if (q0 >= len) return;
     const int64_t qi = q0 + threadIdx.x;
     const bool active = qi < len;
     const int64_t ld = (int64_t)a.heads * HD;   // token stride in floats
     const float* Q = reinterpret_cast<const float*>(a.q) + s0 * ld + (int64_t)head * HD;
-    const float* K = reinterpret_cast<const float*>(a.k) + s0 * ld + (int64_t)head * HD;
-    const float* V = reinterpret_cast<const float*>(a.v) + s0 * ld + (int64_t)head * HD;
+    const float* K = reinterpret_cast<const float*>(a.k) + k0 * ld + (int64_t)head * HD;
+    const float* V = reinterpret_cast<const float*>(a.v) + k0 * ld + (int64_t)head * HD;
 
     float q[HD], o[HD];
     const int64_t qrow = active ? qi : 0;
@@ -54,12 +60,12 @@ __global__ __launch_bounds__(kQ) void attn_f32_kernel(AttnArgs a) {
     }
     float m = -INFINITY, l = 0.f;
 
-    for (int64_t k0 = 0; k0 < len; k0 += kK) {
-        const int nk = (int)((len - k0) < kK ? (len - k0) : kK);
+    for (int64_t kt = 0; kt < klen; kt += kK) {
+        const int nk = (int)((klen - kt) < kK ? (klen - kt) : kK);
         __syncthreads();
         for (int idx = threadIdx.x; idx < kK * HD; idx += kQ) {
             const int r = idx / HD, d = idx % HD;
-            const int64_t kr = k0 + (r < nk ? r : 0);
+            const int64_t kr = kt + (r < nk ? r : 0);
             ks[r][d] = K[kr * ld + d];
             vs[r][d] = V[kr * ld + d];
         }
@@ -90,9 +96,11 @@ __global__ __launch_bounds__(kQ) void attn_f32_kernel(AttnArgs a) {
     }
     if (active) {
         float* O = reinterpret_cast<float*>(a.o) + s0 * ld + (int64_t)head * HD;
-        const float inv = 1.0f / l;
+        // no keys: the empty sum gives o = 0 and lse = -inf
+        const float inv = klen > 0 ? 1.0f / l : 0.0f;
 #pragma unroll
         for (int d = 0; d < HD; ++d) O[qi * ld + d] = o[d] * inv;
+        if (a.lse != nullptr) a.lse[(s0 + qi) * a.heads + head] = klen > 0 ? m + logf(l) : -INFINITY;
     }
 }
 

@@ -5,13 +5,16 @@
  *   dit_adaln_modulate   y  = gamma * LayerNorm(x) + beta            (adaLN-Zero)
  *   dit_rope3d           q, k <- R_3D(t', h', w') q, k               (3D-RoPE)
  *   dit_attn3d           o  = softmax(q k^T / sqrt(d_head)) v        (full 3D attention)
+ *   dit_attn3d_lse       o, lse over a separate key block per sequence (ring step)
+ *   dit_attn_merge       fold a partial (o, lse) into a float32 accumulator
  *   dit_gated_residual   x' = x + alpha * o   [+ fused Euler pass]   (gated residual)
  *   rf_euler_step        z' = z + dt * u                             (rectified-flow Euler)
  *
  * Definitions come from the pages "DiT, Flow Matching e 3D Attention: A Engenharia
  * de Video com IA" (sections "A ruptura da U-Net", "Flow Matching e Rectified Flow",
- * "3D-RoPE e atencao espaco-temporal") and "Por que e absurdamente dificil gerar um
- * filme inteiro usando IA" (section "Matematica por tras").
+ * "3D-RoPE e atencao espaco-temporal", "Engenharia de inferencia e paralelismo de
+ * contexto: Ulysses, Ring Attention e FP8") and "Por que e absurdamente dificil
+ * gerar um filme inteiro usando IA" (section "Matematica por tras").
  *
  * Layout (every activation tensor is token-major and contiguous):
  *   hidden x, y, branch      [tokens][d_model]
@@ -123,6 +126,53 @@ int dit_attn3d(void* o, const void* q, const void* k, const void* v,
                int64_t tokens, int32_t heads, int32_t head_dim,
                const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
                int32_t dtype, void* stream);
+
+/*
+ * One ring-attention step ("DiT, Flow Matching e 3D Attention", section
+ * "Engenharia de inferencia e paralelismo de contexto: Ulysses, Ring Attention e
+ * FP8"): each sequence's queries attend to that sequence's key/value block, and
+ * the row log-sum-exp is returned so that blocks can be merged
+ * (dit_attn_merge). For query i of sequence s and head h, over the keys j of
+ * the sequence's block, with s_j = q[i][h] . k[j][h] / sqrt(head_dim):
+ *   lse[i][h] = ln sum_j exp(s_j)           (natural log, float32)
+ *   o[i][h]   = sum_j exp(s_j - lse[i][h]) v[j][h]
+ * A sequence whose block has no keys gives o = 0 and lse = -inf.
+ *
+ *   o, q          [tokens_q][heads][head_dim] (dtype); o must not overlap q, k, v
+ *   k, v          [tokens_k][heads][head_dim] (dtype)
+ *   lse           [tokens_q][heads] float32; must not overlap o, q, k or v
+ *   dense mode  (cu_seqlens_q == cu_seqlens_k == NULL): num_seqs sequences of
+ *                tokens_q/num_seqs queries and tokens_k/num_seqs keys
+ *   packed mode (both non-NULL): device int32 [num_seqs+1] each; sequence s has
+ *                queries cu_seqlens_q[s]..cu_seqlens_q[s+1] and keys
+ *                cu_seqlens_k[s]..cu_seqlens_k[s+1]; max_seqlen_q / max_seqlen_k
+ *                must be >= every query / key count (unchecked precondition);
+ *                key counts may be 0
+ *   head_dim in {64, 128} (else DIT_E_UNSUPPORTED); tokens_q, tokens_k >= 1
+ * Arithmetic as dit_attn3d, which is the case k, v = the queries' own tokens.
+ */
+int dit_attn3d_lse(void* o, float* lse, const void* q, const void* k, const void* v,
+                   int64_t tokens_q, int64_t tokens_k, int32_t heads, int32_t head_dim,
+                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                   int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t dtype, void* stream);
+
+/*
+ * Fold a partial attention over one key block into a running accumulator over
+ * the blocks seen so far (same section as dit_attn3d_lse): for every
+ * (token, head) row,
+ *   lse_acc' = ln(exp(lse_acc) + exp(lse_b))
+ *   o_acc'   = exp(lse_acc - lse_acc') o_acc + exp(lse_b - lse_acc') o_b
+ * in place. An empty accumulator is o_acc = 0, lse_acc = -inf (merging into it
+ * copies the partial); rows with lse_acc = lse_b = -inf stay o = 0, lse = -inf.
+ *
+ *   o_acc         [tokens][heads][head_dim] float32, read and written
+ *   lse_acc       [tokens][heads] float32, read and written
+ *   o_b           [tokens][heads][head_dim] (dtype: the partial's storage)
+ *   lse_b         [tokens][heads] float32
+ *   head_dim in {64, 128}; no two of the four arrays may overlap
+ */
+int dit_attn_merge(float* o_acc, float* lse_acc, const void* o_b, const float* lse_b,
+                   int64_t tokens, int32_t heads, int32_t head_dim, int32_t dtype, void* stream);
 
 /* Optional Euler pass fused into dit_gated_residual (same launch, same dtype). */
 typedef struct {

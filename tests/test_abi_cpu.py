@@ -22,8 +22,8 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for n in ("dit_adaln_modulate", "dit_rope3d", "dit_attn3d", "dit_gated_residual",
-              "rf_euler_step", "dit_last_error", "dit_version"):
+    for n in ("dit_adaln_modulate", "dit_rope3d", "dit_attn3d", "dit_attn3d_lse", "dit_attn_merge",
+              "dit_gated_residual", "rf_euler_step", "dit_last_error", "dit_version"):
         assert n in names
     assert set(names) == set(dit.EXPORTS)
 
@@ -80,13 +80,49 @@ def test_attn_validation():
     o, q, k, v = FAKE * 16, FAKE, FAKE * 4, FAKE * 8
     assert L.dit_attn3d(None, q, k, v, 64, 2, 128, None, 1, 0, 1, None) == dit.DIT_E_INVAL
     assert L.dit_attn3d(o, q, k, v, 65, 2, 128, None, 2, 0, 1, None) == dit.DIT_E_INVAL
-    assert "multiple of num_seqs" in _err()
+    assert "multiples of num_seqs" in _err()
     assert L.dit_attn3d(o, q, k, v, 64, 2, 96, None, 1, 0, 1, None) == dit.DIT_E_UNSUPPORTED
     assert L.dit_attn3d(o, q, k, v, 64, 2, 128, FAKE * 32, 2, 0, 1, None) == dit.DIT_E_INVAL
     assert "max_seqlen" in _err()
     assert L.dit_attn3d(q, q, k, v, 64, 2, 128, None, 1, 0, 1, None) == dit.DIT_E_INVAL
     assert "overlap" in _err()
     assert L.dit_attn3d(o, q, k, v, 0, 2, 128, None, 1, 0, 1, None) == dit.DIT_E_INVAL
+
+
+def test_attn_lse_validation():
+    L = ensure_built()
+    o, lse, q, k, v = FAKE * 16, FAKE * 24, FAKE, FAKE * 4, FAKE * 8
+    cu_q, cu_k = FAKE * 32, FAKE * 33
+
+    def call(**kw):
+        a = dict(o=o, lse=lse, q=q, k=k, v=v, tq=64, tk=48, h=2, hd=128, cq=None, ck=None, ns=1,
+                 mq=0, mk=0, dtype=1)
+        a.update(kw)
+        return L.dit_attn3d_lse(a["o"], a["lse"], a["q"], a["k"], a["v"], a["tq"], a["tk"], a["h"], a["hd"],
+                                a["cq"], a["ck"], a["ns"], a["mq"], a["mk"], a["dtype"], None)
+    assert call(lse=None) == dit.DIT_E_INVAL and "NULL" in _err()
+    assert call(tk=0) == dit.DIT_E_INVAL
+    assert call(cq=cu_q) == dit.DIT_E_INVAL and "both" in _err()
+    assert call(tk=47, ns=2, tq=64) == dit.DIT_E_INVAL and "multiples" in _err()
+    assert call(cq=cu_q, ck=cu_k, ns=2, mq=0, mk=10) == dit.DIT_E_INVAL and "max_seqlen" in _err()
+    assert call(cq=cu_q, ck=cu_k, ns=2, mq=32, mk=49) == dit.DIT_E_INVAL and "key" in _err()
+    assert call(hd=96) == dit.DIT_E_UNSUPPORTED
+    assert call(lse=FAKE * 24 + 2) == dit.DIT_E_UNSUPPORTED and "lse" in _err()
+    assert call(lse=q + 64) == dit.DIT_E_INVAL and "lse must not overlap" in _err()
+    assert call(o=k + 32) == dit.DIT_E_INVAL and "overlap" in _err()
+    assert call(dtype=5) == dit.DIT_E_UNSUPPORTED
+
+
+def test_attn_merge_validation():
+    L = ensure_built()
+    oa, la, ob, lb = FAKE, FAKE * 16, FAKE * 32, FAKE * 48
+    assert L.dit_attn_merge(None, la, ob, lb, 8, 2, 64, 1, None) == dit.DIT_E_INVAL
+    assert L.dit_attn_merge(oa, la, ob, lb, 0, 2, 64, 1, None) == dit.DIT_E_INVAL
+    assert L.dit_attn_merge(oa, la, ob, lb, 8, 2, 32, 1, None) == dit.DIT_E_UNSUPPORTED
+    assert L.dit_attn_merge(oa + 8, la, ob, lb, 8, 2, 64, 1, None) == dit.DIT_E_UNSUPPORTED
+    assert L.dit_attn_merge(oa, oa + 64, ob, lb, 8, 2, 64, 1, None) == dit.DIT_E_INVAL
+    assert "overlap" in _err()
+    assert L.dit_attn_merge(oa, la, ob, lb, 8, 2, 64, 9, None) == dit.DIT_E_UNSUPPORTED
 
 
 def test_epilogue_validation():

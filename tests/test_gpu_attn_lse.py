@@ -1,0 +1,238 @@
+"""GPU parity of the ring-attention building blocks -- attention of each
+sequence's queries against a separate key block with the row log-sum-exp
+(dit_attn3d_lse), and the fold of a partial into a float32 accumulator
+(dit_attn_merge) -- against the float64 oracle, through the C-ABI binding.
+
+Tolerances (max-abs against the unrounded oracle):
+  o    as dit_attn3d: 2e-2 bf16, 1e-4 float32; a merged accumulator carries
+       one bf16 rounding per partial (each partial is stored in bf16), never a
+       rounding of the sum, so the same 2e-2 applies.
+  lse  bf16: 4e-3. The row sum l is accumulated from probabilities rounded to
+       bf16 (relative error <= 2^-9 each, hence <= 2^-9 for the sum), so
+       ln l moves by at most 2^-9 ~ 0.002; twice that for float32 noise.
+       float32: 1e-4.
+  merge alone (float32 arithmetic on stored inputs): 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_video_amd as dit
+import synth
+from gpu_util import TOL, host64, maxabs, need_gpu, note, sample_rows
+from oracle import attention as o_attn
+
+pytestmark = pytest.mark.gpu
+
+TOL_LSE = {"bf16": 4e-3, "f32": 1e-4}
+TOL_MERGE = 1e-5
+
+
+def _tensors(seed, n, heads, hd, dtype):
+    r = np.random.default_rng(seed)
+    a = r.standard_normal((n, heads, hd)).astype(np.float32)
+    if dtype == "bf16":
+        a = synth.bf16_round(a)
+    return a
+
+
+def _dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(
+        torch.bfloat16 if dtype == "bf16" else torch.float32).cuda()
+
+
+def _cu(lens):
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+
+
+def _attn_lse(q, k, v, cu_q, cu_k, dtype):
+    heads = q.shape[1]
+    qd, kd, vd = _dev(q, dtype), _dev(k, dtype), _dev(v, dtype)
+    o = torch.empty_like(qd)
+    lse = torch.empty(q.shape[0], heads, dtype=torch.float32, device="cuda")
+    cq = torch.from_numpy(cu_q).cuda()
+    ck = torch.from_numpy(cu_k).cuda()
+    dit.dit_attn3d_lse(o, lse, qd, kd, vd, cq, ck, max_seqlen_q=int(np.diff(cu_q).max()),
+                       max_seqlen_k=int(np.diff(cu_k).max()))
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _check_lse(o, lse, q, k, v, cu_q, cu_k, dtype, rows=None):
+    ref_o, ref_l = o_attn.attention_lse(q, k, v, cu_q, cu_k, rows=rows)
+    got_o = host64(o) if rows is None else host64(o[torch.from_numpy(rows).cuda()])
+    got_l = host64(lse) if rows is None else host64(lse[torch.from_numpy(rows).cuda()])
+    empty = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(got_l), empty), "empty key sets must give lse = -inf exactly"
+    assert np.all(got_o[empty] == 0.0), "empty key sets must give o = 0 exactly"
+    e_o = maxabs(got_o, ref_o)
+    e_l = maxabs(got_l[~empty], ref_l[~empty])
+    note(f"attn_lse {dtype} {q.shape}x{k.shape}: o {e_o:.3e} lse {e_l:.3e}")
+    assert e_o <= TOL[dtype] and e_l <= TOL_LSE[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("hd", [64, 128])
+def test_ragged_query_and_key_sets(dtype, hd):
+    """Query and key counts differ per sequence, none a multiple of a tile, one
+    key set empty, one sequence with a single key."""
+    need_gpu()
+    lq, lk = [37, 300, 1, 129], [70, 0, 513, 1]
+    q = _tensors(1, sum(lq), 3, hd, dtype)
+    k = _tensors(2, sum(lk), 3, hd, dtype)
+    v = _tensors(3, sum(lk), 3, hd, dtype)
+    cu_q, cu_k = _cu(lq), _cu(lk)
+    o, lse = _attn_lse(q, k, v, cu_q, cu_k, dtype)
+    _check_lse(o, lse, q, k, v, cu_q, cu_k, dtype)
+
+
+def test_dense_mode_lse():
+    need_gpu()
+    q = _tensors(4, 2 * 200, 2, 128, "bf16")
+    k = _tensors(5, 2 * 333, 2, 128, "bf16")
+    v = _tensors(6, 2 * 333, 2, 128, "bf16")
+    o = torch.empty(400, 2, 128, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(400, 2, dtype=torch.float32, device="cuda")
+    dit.dit_attn3d_lse(o, lse, _dev(q, "bf16"), _dev(k, "bf16"), _dev(v, "bf16"), num_seqs=2)
+    torch.cuda.synchronize()
+    _check_lse(o, lse, q, k, v, _cu([200, 200]), _cu([333, 333]), "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_self_attention_matches_attn3d_bitwise(dtype):
+    """With each sequence's keys its own tokens, o is bit-identical to dit_attn3d."""
+    need_gpu()
+    lens = [300, 77, 512]
+    q, k, v = (_tensors(7 + i, sum(lens), 2, 128, dtype) for i in range(3))
+    cu = _cu(lens)
+    o, lse = _attn_lse(q, k, v, cu, cu, dtype)
+    ref = torch.empty_like(o)
+    dit.dit_attn3d(ref, _dev(q, dtype), _dev(k, dtype), _dev(v, dtype), torch.from_numpy(cu).cuda(),
+                   max_seqlen=max(lens))
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref)
+    assert bool(torch.isfinite(lse).all())
+
+
+def _merge_all(parts, tokens, heads, hd):
+    acc = torch.zeros(tokens, heads, hd, dtype=torch.float32, device="cuda")
+    lacc = torch.full((tokens, heads), float("-inf"), dtype=torch.float32, device="cuda")
+    for o, lse in parts:
+        dit.dit_attn_merge(acc, lacc, o, lse)
+    torch.cuda.synchronize()
+    return acc, lacc
+
+
+def test_merge_against_oracle():
+    """Random accumulators and partials, including empty rows on either side and
+    on both, bf16 and float32 partials, in place."""
+    need_gpu()
+    r = np.random.default_rng(12)
+    n, h, hd = 257, 3, 128
+    for dtype in ("bf16", "f32"):
+        oa = r.standard_normal((n, h, hd)).astype(np.float32)
+        ob = r.standard_normal((n, h, hd)).astype(np.float32)
+        if dtype == "bf16":
+            ob = synth.bf16_round(ob)
+        la = (r.standard_normal((n, h)) * 5).astype(np.float32)
+        lb = (r.standard_normal((n, h)) * 5).astype(np.float32)
+        la[:5] = -np.inf
+        oa[:5] = 0.0
+        lb[3:9] = -np.inf
+        ob[3:9] = 0.0
+        acc = torch.from_numpy(oa).cuda()
+        lacc = torch.from_numpy(la).cuda()
+        dit.dit_attn_merge(acc, lacc, _dev(ob, dtype), torch.from_numpy(lb).cuda())
+        torch.cuda.synchronize()
+        ref_o, ref_l = o_attn.merge(oa, la, ob, lb)
+        got_l = host64(lacc)
+        assert np.array_equal(np.isneginf(got_l), np.isneginf(ref_l))
+        live = np.isfinite(ref_l)
+        e_o = maxabs(host64(acc), ref_o)
+        e_l = maxabs(got_l[live], ref_l[live])
+        note(f"merge {dtype}: o {e_o:.3e} lse {e_l:.3e}")
+        assert e_o <= TOL_MERGE and e_l <= TOL_MERGE
+
+
+def test_split_merge_ragged_equals_full():
+    """Keys of every sequence split at ragged points (one part empty for one
+    sequence); merging the parts equals attention over all keys, against the
+    oracle and against dit_attn3d."""
+    need_gpu()
+    lens = [130, 64, 999, 5]
+    cuts = [(50, 130), (0, 64), (333, 700), (5, 5)]   # three parts per sequence
+    q, k, v = (_tensors(20 + i, sum(lens), 2, 128, "bf16") for i in range(3))
+    cu = _cu(lens)
+    parts = []
+    for part in range(3):
+        idx, plen = [], []
+        for s, (a, b) in enumerate(cuts):
+            lo = [0, a, b][part]
+            hi = [a, b, lens[s]][part]
+            idx += list(range(cu[s] + lo, cu[s] + hi))
+            plen.append(hi - lo)
+        idx = np.asarray(idx, dtype=np.int64)
+        parts.append(_attn_lse(q, k[idx], v[idx], cu, _cu(plen), "bf16"))
+    acc, lacc = _merge_all(parts, sum(lens), 2, 128)
+    ref_o, ref_l = o_attn.attention_lse(q, k, v, cu, cu)
+    e_o, e_l = maxabs(host64(acc), ref_o), maxabs(host64(lacc), ref_l)
+    full = torch.empty(sum(lens), 2, 128, dtype=torch.bfloat16, device="cuda")
+    dit.dit_attn3d(full, _dev(q, "bf16"), _dev(k, "bf16"), _dev(v, "bf16"), torch.from_numpy(cu).cuda(),
+                   max_seqlen=max(lens))
+    torch.cuda.synchronize()
+    e_f = maxabs(host64(acc), host64(full))
+    note(f"split/merge ragged: o {e_o:.3e} lse {e_l:.3e} vs attn3d {e_f:.3e}")
+    assert e_o <= TOL["bf16"] and e_l <= TOL_LSE["bf16"] and e_f <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("w", [synth.C3, synth.C5], ids=lambda w: w.name)
+def test_full_size_ring_of_four(w):
+    """A ring of four steps at the workload's full size: each sequence's keys in
+    four contiguous blocks (ragged split points), one dit_attn3d_lse per block,
+    folded with dit_attn_merge; sampled rows against the oracle, every row
+    against dit_attn3d."""
+    need_gpu()
+    inp = synth.make(w, ["q", "k", "v"])
+    q, k, v = (np.asarray(inp[n], dtype=np.float32) for n in ("q", "k", "v"))
+    cu = w.cu_seqlens.astype(np.int64)
+    lens = np.diff(cu)
+    qd = _dev(q, "bf16")
+    kd, vd = _dev(k, "bf16"), _dev(v, "bf16")
+    parts = []
+    for part in range(4):
+        idx, plen = [], []
+        for s in range(w.num_seqs):
+            b = [0, lens[s] // 4 - 3, lens[s] // 2 + 5, (3 * lens[s]) // 4 + 1, lens[s]]
+            idx.append(np.arange(cu[s] + b[part], cu[s] + b[part + 1]))
+            plen.append(b[part + 1] - b[part])
+        idx = torch.from_numpy(np.concatenate(idx)).cuda()
+        kp, vp = kd[idx].contiguous(), vd[idx].contiguous()
+        o = torch.empty_like(qd)
+        lse = torch.empty(w.tokens, w.heads, dtype=torch.float32, device="cuda")
+        cu_k = _cu(plen)
+        dit.dit_attn3d_lse(o, lse, qd, kp, vp, torch.from_numpy(cu.astype(np.int32)).cuda(),
+                           torch.from_numpy(cu_k).cuda(), max_seqlen_q=int(lens.max()),
+                           max_seqlen_k=int(np.diff(cu_k).max()))
+        parts.append((o, lse))
+    acc, lacc = _merge_all(parts, w.tokens, w.heads, w.head_dim)
+    full = torch.empty_like(qd)
+    dit.dit_attn3d(full, qd, kd, vd, torch.from_numpy(cu.astype(np.int32)).cuda(), max_seqlen=int(lens.max()))
+    torch.cuda.synchronize()
+    e_f = maxabs(host64(acc), host64(full))
+    rows = sample_rows(w, per_seq=64)
+    rt = torch.from_numpy(rows).cuda()
+    ref_o, ref_l = o_attn.attention_lse(q, k, v, cu, cu, rows=rows)
+    e_o, e_l = maxabs(host64(acc[rt]), ref_o), maxabs(host64(lacc[rt]), ref_l)
+    note(f"ring of four {w.name}: o {e_o:.3e} lse {e_l:.3e} vs attn3d {e_f:.3e}")
+    assert e_o <= TOL["bf16"] and e_l <= TOL_LSE["bf16"] and e_f <= TOL["bf16"]
+
+
+def test_lse_deterministic():
+    need_gpu()
+    lens, klens = [700, 64], [1000, 3]
+    q = _tensors(30, sum(lens), 2, 128, "bf16")
+    k = _tensors(31, sum(klens), 2, 128, "bf16")
+    v = _tensors(32, sum(klens), 2, 128, "bf16")
+    a = _attn_lse(q, k, v, _cu(lens), _cu(klens), "bf16")
+    b = _attn_lse(q, k, v, _cu(lens), _cu(klens), "bf16")
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
