@@ -52,3 +52,45 @@ def interpolant(x0: np.ndarray, x1: np.ndarray, t) -> np.ndarray:
 def velocity(x0: np.ndarray, x1: np.ndarray) -> np.ndarray:
     """d/dt x_t = x_1 - x_0 for the linear path."""
     return np.asarray(x1, dtype=np.float64) - np.asarray(x0, dtype=np.float64)
+
+
+def _rows(n: int, tokens_per_row: int) -> np.ndarray:
+    return np.arange(n) // int(tokens_per_row)
+
+
+def interpolant_rows(x0: np.ndarray, x1: np.ndarray, t_rows: np.ndarray,
+                     tokens_per_row: int) -> np.ndarray:
+    """Training input of the straight path ("DiT, Flow Matching e 3D Attention",
+    section "Flow Matching e Rectified Flow"): x_t = (1 - t) x_0 + t x_1 with one
+    flow time per row (sample or frame), row = token // tokens_per_row."""
+    x0 = np.asarray(x0, dtype=np.float64)
+    t = np.asarray(t_rows, dtype=np.float64)[_rows(x0.shape[0], tokens_per_row)]
+    return interpolant(x0, x1, t)
+
+
+def cfm_loss(u: np.ndarray, x0: np.ndarray, x1: np.ndarray, tokens_per_row: int):
+    """Conditional flow-matching regression target (same section): the squared
+    distance between the predicted velocity u and the path's velocity x_1 - x_0.
+
+    Returns (per_token, per_row): per_token[tok] = sum over the token's channels
+    of (u - (x_1 - x_0))^2; per_row[r] = sum of per_token over the row's tokens,
+    i.e. the squared norm of the whole sample (or frame). The expectation over
+    samples in the page's loss is the mean of per_row over the rows (a reading:
+    the norm is taken over the sample's whole latent, not averaged per element)."""
+    e = np.asarray(u, dtype=np.float64) - velocity(x0, x1)
+    per_tok = (e * e).sum(axis=1)
+    rows = _rows(e.shape[0], tokens_per_row)
+    per_row = np.zeros(int(rows[-1]) + 1 if len(rows) else 0, dtype=np.float64)
+    np.add.at(per_row, rows, per_tok)
+    return per_tok, per_row
+
+
+def midpoint_half(z: np.ndarray, u: np.ndarray, dt_rows: np.ndarray,
+                  tokens_per_row: int) -> np.ndarray:
+    """First stage of the explicit midpoint rule, the second ODE sampler the same
+    section names beside Euler: z_mid = z + (dt / 2) u(z, t). The step then
+    finishes with z + dt u(z_mid, t + dt / 2) (euler_step with the midpoint
+    velocity)."""
+    z = np.asarray(z, dtype=np.float64)
+    dt = np.asarray(dt_rows, dtype=np.float64)[_rows(z.shape[0], tokens_per_row)]
+    return z + 0.5 * dt[:, None] * np.asarray(u, dtype=np.float64)

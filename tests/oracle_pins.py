@@ -38,6 +38,7 @@ def real_impl():
         attention_lse=o_attn.attention_lse, merge=o_attn.merge,
         gated_residual=o_epi.gated_residual, euler_step=o_epi.euler_step,
         interpolant=o_epi.interpolant, velocity=o_epi.velocity,
+        interpolant_rows=o_epi.interpolant_rows, cfm_loss=o_epi.cfm_loss, midpoint_half=o_epi.midpoint_half,
     )
 
 
@@ -482,6 +483,85 @@ def pin_euler_30_steps(impl):
     for _ in range(30):
         z = impl.euler_step(z, u, np.full(3, 1.0 / 30.0), 1)
     assert np.allclose(z, x1, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------ CFM loss, midpoint sampler
+def pin_interpolant_rows_endpoints(impl):
+    """t = 0 gives the noise, t = 1 the data, t = 1/2 the average, per row."""
+    r = _rng(50)
+    x0, x1 = r.standard_normal((12, 8)), r.standard_normal((12, 8))
+    xt = impl.interpolant_rows(x0, x1, np.array([0.0, 1.0, 0.5]), 4)
+    assert np.array_equal(xt[:4], x0[:4]) and np.array_equal(xt[4:8], x1[4:8])
+    assert np.allclose(xt[8:], (x0[8:] + x1[8:]) / 2, atol=1e-15)
+
+
+def pin_cfm_exact_velocity_zero(impl):
+    """The path's own velocity has zero loss, exactly."""
+    r = _rng(51)
+    x0, x1 = r.standard_normal((10, 16)), r.standard_normal((10, 16))
+    per_tok, per_row = impl.cfm_loss(x1 - x0, x0, x1, 5)
+    assert np.all(per_tok == 0.0) and np.all(per_row == 0.0)
+
+
+def pin_cfm_bruteforce(impl):
+    """Per-token and per-row sums against loops over (token, channel)."""
+    r = _rng(52)
+    u, x0, x1 = (r.standard_normal((9, 5)) for _ in range(3))
+    per_tok, per_row = impl.cfm_loss(u, x0, x1, 3)
+    for tok in range(9):
+        acc = 0.0
+        for c in range(5):
+            d = u[tok, c] - x1[tok, c] + x0[tok, c]
+            acc += d * d
+        assert abs(per_tok[tok] - acc) < 1e-12
+    for row in range(3):
+        assert abs(per_row[row] - sum(per_tok[3 * row + i] for i in range(3))) < 1e-12
+    assert per_row.shape == (3,)
+
+
+def pin_cfm_translation_and_scale(impl):
+    """Shifting noise and data together leaves the loss unchanged; doubling the
+    velocity error quadruples it."""
+    r = _rng(53)
+    x0, x1, e = (r.standard_normal((6, 4)) for _ in range(3))
+    _, a = impl.cfm_loss(x1 - x0 + e, x0, x1, 3)
+    _, b = impl.cfm_loss(x1 - x0 + e, x0 + 7.0, x1 + 7.0, 3)
+    _, c = impl.cfm_loss(x1 - x0 + 2 * e, x0, x1, 3)
+    assert np.allclose(a, b, rtol=1e-12) and np.allclose(c, 4 * a, rtol=1e-12)
+
+
+def _midpoint_solve(impl, z0, lam, n):
+    """Integrate dz/dt = lam(t) z on [0, 1] with n explicit-midpoint steps."""
+    dt = 1.0 / n
+    z = z0.copy()
+    for i in range(n):
+        t = i * dt
+        zm = impl.midpoint_half(z, lam(t) * z, np.array([dt]), len(z))
+        z = impl.euler_step(z, lam(t + dt / 2) * zm, np.array([dt]), len(z))
+    return z
+
+
+def pin_midpoint_second_order(impl):
+    """On dz/dt = lam(t) z (closed form z0 exp(int lam)) the midpoint sampler's
+    error falls 4x when the step halves (second order; Euler's falls 2x)."""
+    lam = lambda t: math.cos(3.0 * t) - 0.5
+    z0 = np.array([[1.0, -2.0], [0.5, 3.0]])
+    exact = z0 * math.exp(math.sin(3.0) / 3.0 - 0.5)
+    e1 = np.abs(_midpoint_solve(impl, z0, lam, 32) - exact).max()
+    e2 = np.abs(_midpoint_solve(impl, z0, lam, 64) - exact).max()
+    assert 3.5 < e1 / e2 < 4.5, e1 / e2
+
+
+def pin_midpoint_straight_path(impl):
+    """Constant velocity x1 - x0 (the straight path): one midpoint step of size
+    1 from the noise lands on the data; the half stage stops at the middle."""
+    r = _rng(54)
+    x0, x1 = r.standard_normal((6, 4)), r.standard_normal((6, 4))
+    u = x1 - x0
+    zm = impl.midpoint_half(x0, u, np.array([1.0, 1.0]), 3)
+    assert np.allclose(zm, (x0 + x1) / 2, atol=1e-15)
+    assert np.allclose(impl.euler_step(x0, u, np.array([1.0, 1.0]), 3), x1, atol=1e-15)
+    assert np.array_equal(impl.midpoint_half(x0, u, np.zeros(2), 3), x0)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

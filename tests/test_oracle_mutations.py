@@ -114,6 +114,26 @@ def _merge_with(swap_weights=False, no_renorm=False):
     return f
 
 
+def _cfm_with(abs_err=False, plus=False, mean=False):
+    def f(u, x0, x1, tpr):
+        v = np.asarray(x1, np.float64) + np.asarray(x0, np.float64) if plus else \
+            np.asarray(x1, np.float64) - np.asarray(x0, np.float64)
+        e = np.asarray(u, np.float64) - v
+        per_tok = np.abs(e).sum(axis=1) if abs_err else (e * e).sum(axis=1)
+        if mean:
+            per_tok = per_tok / e.shape[1]
+        rows = np.arange(len(e)) // tpr
+        per_row = np.zeros(rows[-1] + 1)
+        np.add.at(per_row, rows, per_tok)
+        return per_tok, per_row
+    return f
+
+
+def _midpoint_full_step(z, u, dt, tpr):
+    rows = np.arange(len(z)) // tpr
+    return np.asarray(z, np.float64) + np.asarray(dt, np.float64)[rows][:, None] * u
+
+
 def _coords_swapped(n, gh, gw):
     n = np.asarray(n, dtype=np.int64)
     return np.stack([n // (gh * gw), n % gw, (n // gw) % gh], axis=-1)
@@ -162,6 +182,10 @@ MUTANTS = {
     "lse_max_only": dict(attention_lse=_lse_with(lse_of_max=True)),
     "merge_swapped_weights": dict(merge=_merge_with(swap_weights=True)),
     "merge_no_renormalise": dict(merge=_merge_with(no_renorm=True)),
+    "cfm_abs_error": dict(cfm_loss=_cfm_with(abs_err=True)),
+    "cfm_wrong_velocity_sign": dict(cfm_loss=_cfm_with(plus=True)),
+    "cfm_mean_not_norm": dict(cfm_loss=_cfm_with(mean=True)),
+    "midpoint_full_step": dict(midpoint_half=_midpoint_full_step),
     "grid_h_w_swapped": dict(coords=_coords_swapped),
     "interpolant_reversed": dict(interpolant=_interp_reversed),
     "euler_wrong_sign": dict(euler_step=_euler_minus),
