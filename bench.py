@@ -226,6 +226,22 @@ def main():
                                     for i in range(R)])
     del accs, laccs, obs, lbs
 
+    # flow-matching training side (not part of the sampling step): the straight-path
+    # interpolant and the flow-matching loss over the latent
+    P_ = synth.LATENT_CHANNELS
+    R = rotation(3 * w.tokens * P_ * esz)
+    x0s = [z.clone() for _ in range(R)]
+    x1s = [u.clone() for _ in range(R)]
+    xts = [torch.empty_like(z) for _ in range(R)]
+    trows = torch.rand(w.rows, dtype=torch.float32, device="cuda")
+    kern_ms["interpolant"] = timed_batch([
+        (lambda i=i: dit.rf_interpolant(xts[i], x0s[i], x1s[i], trows, w.tokens_per_row)) for i in range(R)])
+    ltok = [torch.empty(w.tokens, dtype=torch.float32, device="cuda") for _ in range(R)]
+    lrow = [torch.empty(w.rows, dtype=torch.float32, device="cuda") for _ in range(R)]
+    kern_ms["cfm_loss"] = timed_batch([
+        (lambda i=i: dit.rf_cfm_loss(ltok[i], lrow[i], xts[i], x0s[i], x1s[i], w.tokens_per_row)) for i in range(R)])
+    del x0s, x1s, xts, ltok, lrow
+
     flops = w.attn_flops()
     tok, D, P = w.tokens, w.d_model, synth.LATENT_CHANNELS
     algo_bytes = {
@@ -233,6 +249,8 @@ def main():
         "rope": 4 * tok * D * esz,
         "residual_euler": 3 * tok * D * esz + 3 * tok * P * esz,
         "merge": merge_bytes,
+        "interpolant": 3 * tok * P * esz,
+        "cfm_loss": 3 * tok * P * esz + tok * 4 + w.rows * 4,
     }
     attn_s = kern_ms["attn"] * 1e-3
     achieved = flops / attn_s / 1e12

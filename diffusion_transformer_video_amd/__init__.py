@@ -27,7 +27,8 @@ DIT_F32, DIT_BF16 = 0, 1
 DIT_OK, DIT_E_INVAL, DIT_E_UNSUPPORTED, DIT_E_HIP = 0, 1, 2, 3
 
 EXPORTS = ("dit_last_error", "dit_version", "dit_adaln_modulate", "dit_rope3d",
-           "dit_attn3d", "dit_attn3d_lse", "dit_attn_merge", "dit_gated_residual", "rf_euler_step")
+           "dit_attn3d", "dit_attn3d_lse", "dit_attn_merge", "dit_gated_residual", "rf_euler_step",
+           "rf_midpoint_half", "rf_interpolant", "rf_cfm_loss")
 
 
 class DitError(RuntimeError):
@@ -74,6 +75,11 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(EulerArgs), i32, vp]
         L.rf_euler_step.restype = ctypes.c_int
         L.rf_euler_step.argtypes = [vp, vp, vp, vp, i64, i32, i64, i32, vp]
+        for name in ("rf_midpoint_half", "rf_interpolant"):
+            getattr(L, name).restype = ctypes.c_int
+            getattr(L, name).argtypes = [vp, vp, vp, vp, i64, i32, i64, i32, vp]
+        L.rf_cfm_loss.restype = ctypes.c_int
+        L.rf_cfm_loss.argtypes = [vp, vp, vp, vp, vp, i64, i32, i64, i32, vp]
         _lib = L
     return _lib
 
@@ -243,3 +249,44 @@ def rf_euler_step(z_out, z, u, dt_rows, tokens_per_row: int, stream=None):
     _check(lib().rf_euler_step(_ptr(z_out), _ptr(z), _ptr(u), _ptr(dt_rows), tokens, ch,
                                int(tokens_per_row), _dtype_code(z), _stream(stream)))
     return z_out
+
+
+def rf_midpoint_half(z_mid, z, u, dt_rows, tokens_per_row: int, stream=None):
+    """z_mid = z + (dt_rows[row] / 2) * u; z, u [tokens, channels]."""
+    _dev(z_mid, z, u, dt_rows)
+    _f32(dt_rows)
+    if z.dim() != 2 or z_mid.shape != z.shape or u.shape != z.shape or u.dtype != z.dtype or z_mid.dtype != z.dtype:
+        raise ValueError("z, z_mid, u must be [tokens, channels] of one dtype")
+    tokens, ch = z.shape
+    _check(lib().rf_midpoint_half(_ptr(z_mid), _ptr(z), _ptr(u), _ptr(dt_rows), tokens, ch,
+                                  int(tokens_per_row), _dtype_code(z), _stream(stream)))
+    return z_mid
+
+
+def rf_interpolant(x_t, x0, x1, t_rows, tokens_per_row: int, stream=None):
+    """x_t = (1 - t[row]) x0 + t[row] x1; x0, x1 [tokens, channels]."""
+    _dev(x_t, x0, x1, t_rows)
+    _f32(t_rows)
+    if x0.dim() != 2 or x1.shape != x0.shape or x_t.shape != x0.shape or \
+            x1.dtype != x0.dtype or x_t.dtype != x0.dtype:
+        raise ValueError("x_t, x0, x1 must be [tokens, channels] of one dtype")
+    tokens, ch = x0.shape
+    _check(lib().rf_interpolant(_ptr(x_t), _ptr(x0), _ptr(x1), _ptr(t_rows), tokens, ch,
+                                int(tokens_per_row), _dtype_code(x0), _stream(stream)))
+    return x_t
+
+
+def rf_cfm_loss(loss_tokens, loss_rows, u, x0, x1, tokens_per_row: int, stream=None):
+    """loss_tokens[tok] = sum_c (u - (x1 - x0))^2; loss_rows (or None) the per-row sums."""
+    _dev(loss_tokens, loss_rows, u, x0, x1)
+    _f32(loss_tokens, *(() if loss_rows is None else (loss_rows,)))
+    if u.dim() != 2 or x0.shape != u.shape or x1.shape != u.shape or x0.dtype != u.dtype or x1.dtype != u.dtype:
+        raise ValueError("u, x0, x1 must be [tokens, channels] of one dtype")
+    tokens, ch = u.shape
+    if loss_tokens.shape != (tokens,):
+        raise ValueError("loss_tokens must be [tokens]")
+    if loss_rows is not None and loss_rows.shape != (tokens // int(tokens_per_row),):
+        raise ValueError("loss_rows must be [tokens // tokens_per_row]")
+    _check(lib().rf_cfm_loss(_ptr(loss_tokens), _ptr(loss_rows), _ptr(u), _ptr(x0), _ptr(x1), tokens, ch,
+                             int(tokens_per_row), _dtype_code(u), _stream(stream)))
+    return loss_tokens, loss_rows

@@ -312,4 +312,59 @@ int rf_euler_step(void* z_out, const void* z, const void* u, const float* dt_row
     return launched(dit::launch_epilogue(nullptr, &ea, dtype == DIT_BF16, (hipStream_t)stream), fn);
 }
 
+int rf_midpoint_half(void* z_mid, const void* z, const void* u, const float* dt_rows,
+                     int64_t tokens, int32_t channels, int64_t tokens_per_row,
+                     int32_t dtype, void* stream) {
+    const char* fn = "rf_midpoint_half";
+    if (int rc = check_dtype(dtype, fn)) return rc;
+    if (int rc = validate_euler(fn, z_mid, z, u, dt_rows, tokens, channels, tokens_per_row, dtype)) return rc;
+    if (int rc = check_device(fn)) return rc;
+    dit::EulerArgs ea{z_mid, z, u, dt_rows, tokens, channels, tokens_per_row, 0.5f};
+    return launched(dit::launch_epilogue(nullptr, &ea, dtype == DIT_BF16, (hipStream_t)stream), fn);
+}
+
+int rf_interpolant(void* x_t, const void* x0, const void* x1, const float* t_rows,
+                   int64_t tokens, int32_t channels, int64_t tokens_per_row,
+                   int32_t dtype, void* stream) {
+    const char* fn = "rf_interpolant";
+    if (int rc = check_dtype(dtype, fn)) return rc;
+    if (!x_t || !x0 || !x1 || !t_rows) return fail(DIT_E_INVAL, "%s: NULL pointer argument", fn);
+    if (int rc = validate_rows(fn, tokens, tokens_per_row)) return rc;
+    if (channels <= 0) return fail(DIT_E_INVAL, "%s: channels must be > 0", fn);
+    if (channels % 8 != 0)
+        return fail(DIT_E_UNSUPPORTED, "%s: channels (%d) must be a multiple of 8", fn, channels);
+    if (!aligned16(x_t) || !aligned16(x0) || !aligned16(x1) || ((uintptr_t)t_rows % 4) != 0)
+        return fail(DIT_E_UNSUPPORTED, "%s: tensors must be 16-byte aligned (t_rows 4-byte)", fn);
+    const int64_t bytes = tokens * channels * elem_size(dtype);
+    if ((x_t != x0 && overlaps(x_t, bytes, x0, bytes)) || (x_t != x1 && overlaps(x_t, bytes, x1, bytes)))
+        return fail(DIT_E_INVAL, "%s: x_t partially overlaps x0 or x1", fn);
+    if (int rc = check_device(fn)) return rc;
+    dit::InterpArgs a{x_t, x0, x1, t_rows, tokens, channels, tokens_per_row};
+    return launched(dit::launch_interpolant(a, dtype == DIT_BF16, (hipStream_t)stream), fn);
+}
+
+int rf_cfm_loss(float* loss_tokens, float* loss_rows, const void* u, const void* x0, const void* x1,
+                int64_t tokens, int32_t channels, int64_t tokens_per_row, int32_t dtype, void* stream) {
+    const char* fn = "rf_cfm_loss";
+    if (int rc = check_dtype(dtype, fn)) return rc;
+    if (!loss_tokens || !u || !x0 || !x1) return fail(DIT_E_INVAL, "%s: NULL pointer argument", fn);
+    if (int rc = validate_rows(fn, tokens, tokens_per_row)) return rc;
+    if (channels <= 0) return fail(DIT_E_INVAL, "%s: channels must be > 0", fn);
+    if (channels % 8 != 0)
+        return fail(DIT_E_UNSUPPORTED, "%s: channels (%d) must be a multiple of 8", fn, channels);
+    if (!aligned16(u) || !aligned16(x0) || !aligned16(x1) || ((uintptr_t)loss_tokens % 4) != 0 ||
+        ((uintptr_t)loss_rows % 4) != 0)
+        return fail(DIT_E_UNSUPPORTED, "%s: inputs must be 16-byte aligned, losses 4-byte", fn);
+    const int64_t bytes = tokens * channels * elem_size(dtype), lb = tokens * 4;
+    const int64_t rb = (tokens / tokens_per_row) * 4;
+    if (overlaps(loss_tokens, lb, u, bytes) || overlaps(loss_tokens, lb, x0, bytes) ||
+        overlaps(loss_tokens, lb, x1, bytes) ||
+        (loss_rows && (overlaps(loss_rows, rb, loss_tokens, lb) || overlaps(loss_rows, rb, u, bytes) ||
+                       overlaps(loss_rows, rb, x0, bytes) || overlaps(loss_rows, rb, x1, bytes))))
+        return fail(DIT_E_INVAL, "%s: outputs must not overlap the inputs or each other", fn);
+    if (int rc = check_device(fn)) return rc;
+    dit::CfmArgs a{loss_tokens, loss_rows, u, x0, x1, tokens, channels, tokens_per_row};
+    return launched(dit::launch_cfm_loss(a, dtype == DIT_BF16, (hipStream_t)stream), fn);
+}
+
 }  // extern "C"

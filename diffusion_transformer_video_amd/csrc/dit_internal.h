@@ -50,6 +50,7 @@ hipError_t launch_attn_merge(const MergeArgs& a, bool bf16, hipStream_t s);
 struct EulerArgs {
     void* z_out; const void* z; const void* u; const float* dt_rows;
     int64_t tokens; int channels; int64_t tokens_per_row;
+    float dt_scale = 1.0f;   // 0.5: the midpoint rule's half step
 };
 struct ResidualArgs {
     void* x_out; const void* x; const void* branch; const float* alpha;
@@ -57,5 +58,19 @@ struct ResidualArgs {
 };
 // residual may have tokens == 0 (Euler only); euler may be NULL.
 hipError_t launch_epilogue(const ResidualArgs* r, const EulerArgs* e, bool bf16, hipStream_t s);
+
+// x_t = (1 - t[row]) x0 + t[row] x1
+struct InterpArgs {
+    void* xt; const void* x0; const void* x1; const float* t_rows;
+    int64_t tokens; int channels; int64_t tokens_per_row;
+};
+hipError_t launch_interpolant(const InterpArgs& a, bool bf16, hipStream_t s);
+
+// loss_tok[tok] = sum_c (u - (x1 - x0))^2; loss_rows (nullable) = per-row sums
+struct CfmArgs {
+    float* loss_tok; float* loss_rows; const void* u; const void* x0; const void* x1;
+    int64_t tokens; int channels; int64_t tokens_per_row;
+};
+hipError_t launch_cfm_loss(const CfmArgs& a, bool bf16, hipStream_t s);
 
 }  // namespace dit

@@ -5,6 +5,8 @@
 //   x_out[tok][c] = x[tok][c] + alpha[row][c] * branch[tok][c]
 // Euler ("Flow Matching e Rectified Flow" section of the same page):
 //   z_out[tok][c] = z[tok][c] + dt_rows[row] * u[tok][c]
+// and, with dt scaled by 1/2, the first stage of the midpoint sampler the same
+// section names beside Euler.
 //
 // Both are HBM-bound streams (6 bytes per bf16 element). The residual runs as
 // column strips: a thread owns one 8-column chunk and walks kTokPerThread
@@ -80,7 +82,7 @@ __device__ __forceinline__ void euler_block(const EulerArgs& e, int64_t blk) {
     for (int i = 0; i < kEulerChunksPerThread; ++i) {
         const int64_t idx = base + (int64_t)i * kThreads;
         if (idx < total) {
-            const float dt = e.dt_rows[(idx / nchunk) / e.tokens_per_row];
+            const float dt = e.dt_rows[(idx / nchunk) / e.tokens_per_row] * e.dt_scale;
             float zf[8], uf[8], o[8];
             zv[i].unpack(zf);
             uv[i].unpack(uf);

@@ -9,6 +9,9 @@
  *   dit_attn_merge       fold a partial (o, lse) into a float32 accumulator
  *   dit_gated_residual   x' = x + alpha * o   [+ fused Euler pass]   (gated residual)
  *   rf_euler_step        z' = z + dt * u                             (rectified-flow Euler)
+ *   rf_midpoint_half     z_mid = z + (dt/2) * u                      (midpoint sampler, stage 1)
+ *   rf_interpolant       x_t = (1 - t) x0 + t x1                     (straight-path input)
+ *   rf_cfm_loss          |u - (x1 - x0)|^2 per token and per row     (flow-matching loss)
  *
  * Definitions come from the pages "DiT, Flow Matching e 3D Attention: A Engenharia
  * de Video com IA" (sections "A ruptura da U-Net", "Flow Matching e Rectified Flow",
@@ -214,6 +217,45 @@ int dit_gated_residual(void* x_out, const void* x, const void* branch, const flo
 int rf_euler_step(void* z_out, const void* z, const void* u, const float* dt_rows,
                   int64_t tokens, int32_t channels, int64_t tokens_per_row,
                   int32_t dtype, void* stream);
+
+/*
+ * First stage of the explicit midpoint sampler, the second ODE sampler "DiT,
+ * Flow Matching e 3D Attention", section "Flow Matching e Rectified Flow", names
+ * beside Euler:
+ *   z_mid = z + (dt_rows[row] / 2) * u,   u = velocity at (z, t)
+ * The step finishes with rf_euler_step(z_out, z, u_mid, dt_rows, ...), u_mid the
+ * velocity at (z_mid, t + dt/2). Arguments as rf_euler_step (z_mid == z allowed).
+ */
+int rf_midpoint_half(void* z_mid, const void* z, const void* u, const float* dt_rows,
+                     int64_t tokens, int32_t channels, int64_t tokens_per_row,
+                     int32_t dtype, void* stream);
+
+/*
+ * Straight-path training input (same section): x_t = (1 - t) x0 + t x1, with
+ * x0 the noise, x1 the data and one flow time per row (sample or frame). t = 0
+ * and t = 1 return x0 and x1 exactly.
+ *   x_t, x0, x1   [tokens][channels] (dtype); x_t may be x0 or x1
+ *   t_rows        [tokens/tokens_per_row] float32
+ *   channels % 8 == 0
+ */
+int rf_interpolant(void* x_t, const void* x0, const void* x1, const float* t_rows,
+                   int64_t tokens, int32_t channels, int64_t tokens_per_row,
+                   int32_t dtype, void* stream);
+
+/*
+ * Conditional flow-matching loss (same section): the squared distance between
+ * the predicted velocity u and the path's velocity x1 - x0,
+ *   loss_tokens[tok] = sum_c (u[tok][c] - (x1[tok][c] - x0[tok][c]))^2
+ *   loss_rows[r]     = sum of loss_tokens over row r's tokens (the sample's or
+ *                      frame's squared norm; the loss estimate is their mean)
+ * float32 arithmetic; deterministic (fixed reduction order).
+ *   u, x0, x1     [tokens][channels] (dtype)
+ *   loss_tokens   [tokens] float32 (output)
+ *   loss_rows     nullable, [tokens/tokens_per_row] float32 (output)
+ *   channels % 8 == 0; outputs must not overlap the inputs or each other
+ */
+int rf_cfm_loss(float* loss_tokens, float* loss_rows, const void* u, const void* x0, const void* x1,
+                int64_t tokens, int32_t channels, int64_t tokens_per_row, int32_t dtype, void* stream);
 
 #ifdef __cplusplus
 }

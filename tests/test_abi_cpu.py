@@ -23,7 +23,8 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("dit_adaln_modulate", "dit_rope3d", "dit_attn3d", "dit_attn3d_lse", "dit_attn_merge",
-              "dit_gated_residual", "rf_euler_step", "dit_last_error", "dit_version"):
+              "dit_gated_residual", "rf_euler_step", "rf_midpoint_half", "rf_interpolant", "rf_cfm_loss",
+              "dit_last_error", "dit_version"):
         assert n in names
     assert set(names) == set(dit.EXPORTS)
 
@@ -136,6 +137,27 @@ def test_epilogue_validation():
     assert L.dit_gated_residual(FAKE, FAKE, FAKE * 4, FAKE * 8, 32, 64, 32, ctypes.byref(bad), 1,
                                 None) == dit.DIT_E_INVAL
     assert "euler" in _err()
+
+
+def test_flow_validation():
+    L = ensure_built()
+    # midpoint half step: the Euler checks
+    assert L.rf_midpoint_half(FAKE, FAKE, FAKE * 4, None, 32, 64, 32, 1, None) == dit.DIT_E_INVAL
+    assert L.rf_midpoint_half(FAKE, FAKE, FAKE, FAKE * 8, 32, 64, 32, 1, None) == dit.DIT_E_INVAL
+    assert L.rf_midpoint_half(FAKE, FAKE, FAKE * 4, FAKE * 8, 32, 60, 32, 1, None) == dit.DIT_E_UNSUPPORTED
+    # interpolant
+    assert L.rf_interpolant(FAKE, FAKE * 4, FAKE * 8, None, 32, 64, 32, 1, None) == dit.DIT_E_INVAL
+    assert L.rf_interpolant(FAKE, FAKE * 4, FAKE * 8, FAKE * 12, 30, 64, 7, 1, None) == dit.DIT_E_INVAL
+    assert L.rf_interpolant(FAKE, FAKE * 4, FAKE * 8, FAKE * 12, 32, 12, 32, 1, None) == dit.DIT_E_UNSUPPORTED
+    assert L.rf_interpolant(FAKE + 64, FAKE, FAKE * 8, FAKE * 12, 32, 64, 32, 1, None) == dit.DIT_E_INVAL
+    assert "overlaps" in _err()
+    # cfm loss
+    assert L.rf_cfm_loss(None, None, FAKE, FAKE * 4, FAKE * 8, 32, 64, 32, 1, None) == dit.DIT_E_INVAL
+    assert L.rf_cfm_loss(FAKE * 12, None, FAKE, FAKE * 4, FAKE * 8, 32, 64, 5, 1, None) == dit.DIT_E_INVAL
+    assert L.rf_cfm_loss(FAKE * 12 + 2, None, FAKE, FAKE * 4, FAKE * 8, 32, 64, 32, 1, None) == dit.DIT_E_UNSUPPORTED
+    assert L.rf_cfm_loss(FAKE + 64, None, FAKE, FAKE * 4, FAKE * 8, 32, 64, 32, 1, None) == dit.DIT_E_INVAL
+    assert "overlap" in _err()
+    assert L.rf_cfm_loss(FAKE * 12, FAKE * 12, FAKE, FAKE * 4, FAKE * 8, 32, 64, 32, 1, None) == dit.DIT_E_INVAL
 
 
 def test_error_text_is_thread_local_and_cleared_on_new_error():
