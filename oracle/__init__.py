@@ -18,13 +18,21 @@ What it follows (pages are cited by title and section):
                  same page, section "3D-RoPE e atenção espaço-temporal".
   * attention -- softmax(q_rot k_rot^T / sqrt(d_head)) V: same section, and
                  "Por que é absurdamente difícil gerar um filme inteiro usando
-                 IA", section "Matemática por trás".
+                 IA", section "Matemática por trás"; the row log-sum-exp and
+                 the merge of partials over key blocks for ring attention:
+                 first page, section "Engenharia de inferência e paralelismo
+                 de contexto: Ulysses, Ring Attention e FP8".
   * epilogue  -- gated residual x + alpha * out (block equations) and the
                  rectified-flow Euler update along u, section "Flow Matching e
-                 Rectified Flow" (x_t = (1 - t) x_0 + t x_1, v = x_1 - x_0).
+                 Rectified Flow" (x_t = (1 - t) x_0 + t x_1, v = x_1 - x_0),
+                 with the interpolant, the flow-matching loss and the midpoint
+                 sampler's half step from the same section.
+  * flowception -- frame insertion with local-time reset and the per-frame
+                 schedule: "Flowception: Temporally Expansive Flow Matching for
+                 Video Generation", technical summary, section 2.
 
 Every function is pinned by tests in tests/test_oracle_*.py against closed
 forms, invariants, library special cases or brute force; none is "parity
 unpinned".
 """
-from . import attention, epilogue, grid, modulate, rope  # noqa: F401
+from . import attention, epilogue, flowception, grid, modulate, rope  # noqa: F401

@@ -21,6 +21,7 @@ import torch
 import oracle
 from oracle import attention as o_attn
 from oracle import epilogue as o_epi
+from oracle import flowception as o_flow
 from oracle import grid as o_grid
 from oracle import modulate as o_mod
 from oracle import rope as o_rope
@@ -39,6 +40,7 @@ def real_impl():
         gated_residual=o_epi.gated_residual, euler_step=o_epi.euler_step,
         interpolant=o_epi.interpolant, velocity=o_epi.velocity,
         interpolant_rows=o_epi.interpolant_rows, cfm_loss=o_epi.cfm_loss, midpoint_half=o_epi.midpoint_half,
+        insert_frames=o_flow.insert_frames, frame_schedule=o_flow.frame_schedule,
     )
 
 
@@ -562,6 +564,94 @@ def pin_midpoint_straight_path(impl):
     assert np.allclose(zm, (x0 + x1) / 2, atol=1e-15)
     assert np.allclose(impl.euler_step(x0, u, np.array([1.0, 1.0]), 3), x1, atol=1e-15)
     assert np.array_equal(impl.midpoint_half(x0, u, np.zeros(2), 3), x0)
+
+
+# ------------------------------------------------ Flowception insertion
+def _packed(seed, frames_per_seq, tpf=3, ch=2):
+    r = _rng(seed)
+    F = sum(frames_per_seq)
+    z = r.standard_normal((F * tpf, ch))
+    t = r.random(F)
+    cu = np.concatenate([[0], np.cumsum(frames_per_seq)]) * tpf
+    return z, t, cu
+
+
+def pin_insert_none_is_identity(impl):
+    z, t, cu = _packed(60, [2, 3, 1])
+    zo, to, co, src = impl.insert_frames(z, t, cu, np.zeros(6, int), np.zeros((0, 2)), 3)
+    assert np.array_equal(zo, z) and np.array_equal(to, t) and np.array_equal(co, cu)
+    assert np.array_equal(src, np.arange(6))
+
+
+def pin_insert_worked_example(impl):
+    """Two sequences of frames A B | C, counts (1, 0 | 2): the result is
+    A n0 B | C n1 n2 with the new frames at time 0 and the offsets grown."""
+    tpf = 2
+    z = np.array([[1.0], [1.5], [2.0], [2.5], [3.0], [3.5]])   # frames A, B, C
+    t = np.array([0.25, 0.5, 0.75])
+    noise = -np.arange(1.0, 7.0).reshape(6, 1)                 # frames n0, n1, n2
+    zo, to, co, src = impl.insert_frames(z, t, [0, 4, 6], [1, 0, 2], noise, tpf)
+    assert np.array_equal(zo[:, 0], [1.0, 1.5, -1.0, -2.0, 2.0, 2.5, 3.0, 3.5, -3.0, -4.0, -5.0, -6.0])
+    assert np.array_equal(to, [0.25, 0.0, 0.5, 0.75, 0.0, 0.0])
+    assert np.array_equal(co, [0, 6, 12])
+    assert np.array_equal(src, [0, -1, 1, 2, -2, -3])
+
+
+def pin_insert_invariants(impl):
+    """Random counts: sizes grow by the counts per sequence; deleting the
+    inserted frames gives back the input; inserted frames hold the noise in
+    order with time 0; no frame crosses into another sequence."""
+    r = _rng(61)
+    fps = [4, 1, 6, 2]
+    z, t, cu = _packed(62, fps, tpf=5, ch=3)
+    counts = r.poisson(0.8, size=sum(fps))
+    noise = r.standard_normal((counts.sum() * 5, 3))
+    zo, to, co, src = impl.insert_frames(z, t, cu, counts, noise, 5)
+    assert len(to) == sum(fps) + counts.sum() and zo.shape == (len(to) * 5, 3)
+    fo = np.concatenate([[0], np.cumsum(fps)])
+    for s in range(4):
+        assert co[s + 1] - co[s] == 5 * (fps[s] + counts[fo[s]:fo[s + 1]].sum())
+        seg = src[co[s] // 5:co[s + 1] // 5]
+        assert set(seg[seg >= 0]) == set(range(fo[s], fo[s + 1]))
+    keep = src >= 0
+    assert np.array_equal(src[keep], np.arange(sum(fps)))
+    assert np.array_equal(zo.reshape(-1, 5, 3)[keep].reshape(-1, 3), z)
+    assert np.array_equal(to[keep], t)
+    new = ~keep
+    assert np.array_equal(-1 - src[new], np.arange(counts.sum()))
+    assert np.array_equal(zo.reshape(-1, 5, 3)[new].reshape(-1, 3), noise) and np.all(to[new] == 0.0)
+
+
+def pin_insert_bruteforce(impl):
+    """Against list splicing: insert each frame's new frames by walking the
+    existing frames from the last to the first and splicing into a list."""
+    r = _rng(63)
+    fps = [3, 2]
+    z, t, cu = _packed(64, fps, tpf=2, ch=1)
+    counts = r.integers(0, 3, size=5)
+    noise = r.standard_normal((counts.sum() * 2, 1))
+    frames = [("x", f) for f in range(5)]
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    for f in reversed(range(5)):
+        for j in reversed(range(counts[f])):
+            frames.insert(f + 1, ("n", starts[f] + j))
+    zo, to, _, src = impl.insert_frames(z, t, cu, counts, noise, 2)
+    for o, (kind, i) in enumerate(frames):
+        blk = z[2 * i:2 * i + 2] if kind == "x" else noise[2 * i:2 * i + 2]
+        assert np.array_equal(zo[2 * o:2 * o + 2], blk)
+        assert src[o] == (i if kind == "x" else -1 - i)
+
+
+def pin_schedule(impl):
+    """Frames step by dt_max until the last step lands exactly on 1; a frame at
+    1 stays; inserted frames (t = 0) take full steps."""
+    dt, tn = impl.frame_schedule(np.array([0.0, 0.5, 1.0 - 1.0 / 64, 1.0]), 1.0 / 30)
+    assert np.allclose(dt, [1 / 30, 1 / 30, 1 / 64, 0.0], rtol=0, atol=1e-15)
+    assert np.allclose(tn, [1 / 30, 0.5 + 1 / 30, 1.0, 1.0], rtol=0, atol=1e-15)
+    t = np.array([0.0, 0.3])
+    for _ in range(40):
+        _, t = impl.frame_schedule(t, 1.0 / 30)
+    assert np.all(t == 1.0)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -134,6 +134,35 @@ def _midpoint_full_step(z, u, dt, tpr):
     return np.asarray(z, np.float64) + np.asarray(dt, np.float64)[rows][:, None] * u
 
 
+def _insert_before(z, t, cu, counts, noise, tpf):
+    """Puts each frame's new frames before it instead of after it."""
+    blocks, t_out, src, cu_out = [], [], [], [0]
+    n = 0
+    for s in range(len(cu) - 1):
+        for f in range(cu[s] // tpf, cu[s + 1] // tpf):
+            for _ in range(int(counts[f])):
+                blocks.append(noise[n * tpf:(n + 1) * tpf]); t_out.append(0.0); src.append(-1 - n); n += 1
+            blocks.append(z[f * tpf:(f + 1) * tpf]); t_out.append(float(t[f])); src.append(f)
+        cu_out.append(len(src) * tpf)
+    return np.concatenate(blocks), np.array(t_out), np.array(cu_out), np.array(src)
+
+
+def _insert_keep_time(z, t, cu, counts, noise, tpf):
+    """Inserted frames inherit the time of the frame before them (no reset)."""
+    zo, to, co, src = P.real_impl().insert_frames(z, t, cu, counts, noise, tpf)
+    to = to.copy()
+    for o in range(1, len(src)):
+        if src[o] < 0:
+            to[o] = to[o - 1]
+    return zo, to, co, src
+
+
+def _schedule_no_clip(t, dt_max):
+    t = np.asarray(t, np.float64)
+    dt = np.full_like(t, dt_max)
+    return dt, t + dt
+
+
 def _coords_swapped(n, gh, gw):
     n = np.asarray(n, dtype=np.int64)
     return np.stack([n // (gh * gw), n % gw, (n // gw) % gh], axis=-1)
@@ -186,6 +215,9 @@ MUTANTS = {
     "cfm_wrong_velocity_sign": dict(cfm_loss=_cfm_with(plus=True)),
     "cfm_mean_not_norm": dict(cfm_loss=_cfm_with(mean=True)),
     "midpoint_full_step": dict(midpoint_half=_midpoint_full_step),
+    "insert_before_frame": dict(insert_frames=_insert_before),
+    "insert_keeps_time": dict(insert_frames=_insert_keep_time),
+    "schedule_overshoots": dict(frame_schedule=_schedule_no_clip),
     "grid_h_w_swapped": dict(coords=_coords_swapped),
     "interpolant_reversed": dict(interpolant=_interp_reversed),
     "euler_wrong_sign": dict(euler_step=_euler_minus),
