@@ -242,6 +242,28 @@ def main():
         (lambda i=i: dit.rf_cfm_loss(ltok[i], lrow[i], xts[i], x0s[i], x1s[i], w.tokens_per_row)) for i in range(R)])
     del x0s, x1s, xts, ltok, lrow
 
+    # Flowception frame insertion (not part of the step): one new noise frame after
+    # every other frame of the batch (frames = H' x W' token planes)
+    tpf = w.grid_hw[0] * w.grid_hw[1]
+    nfr = w.tokens // tpf
+    cnt = torch.zeros(nfr, dtype=torch.int32, device="cuda")
+    cnt[::2] = 1
+    nfo = nfr + int(cnt.sum())
+    ins_bytes = 2 * nfo * tpf * P_ * esz
+    R = rotation(ins_bytes)
+    tfr = torch.rand(nfr, dtype=torch.float32, device="cuda")
+    cu_fr = torch.from_numpy(w.cu_seqlens.astype(np.int32)).cuda()   # whole frames per sequence
+    zs_ = [z.clone() for _ in range(R)]
+    nzs = [torch.randn((nfo - nfr) * tpf, P_, device="cuda").to(tdt) for _ in range(R)]
+    zos = [torch.empty(nfo * tpf, P_, dtype=tdt, device="cuda") for _ in range(R)]
+    tos = [torch.empty(nfo, dtype=torch.float32, device="cuda") for _ in range(R)]
+    cos = [torch.empty_like(cu_fr) for _ in range(R)]
+    sos = [torch.empty(nfo, dtype=torch.int32, device="cuda") for _ in range(R)]
+    kern_ms["insert_frames"] = timed_batch([
+        (lambda i=i: dit.flow_insert_frames(zos[i], tos[i], cos[i], sos[i], zs_[i], tfr, cu_fr, cnt, nzs[i], tpf))
+        for i in range(R)])
+    del zs_, nzs, zos, tos, cos, sos
+
     flops = w.attn_flops()
     tok, D, P = w.tokens, w.d_model, synth.LATENT_CHANNELS
     algo_bytes = {
@@ -251,6 +273,7 @@ def main():
         "merge": merge_bytes,
         "interpolant": 3 * tok * P * esz,
         "cfm_loss": 3 * tok * P * esz + tok * 4 + w.rows * 4,
+        "insert_frames": ins_bytes,
     }
     attn_s = kern_ms["attn"] * 1e-3
     achieved = flops / attn_s / 1e12

@@ -28,7 +28,8 @@ DIT_OK, DIT_E_INVAL, DIT_E_UNSUPPORTED, DIT_E_HIP = 0, 1, 2, 3
 
 EXPORTS = ("dit_last_error", "dit_version", "dit_adaln_modulate", "dit_rope3d",
            "dit_attn3d", "dit_attn3d_lse", "dit_attn_merge", "dit_gated_residual", "rf_euler_step",
-           "rf_midpoint_half", "rf_interpolant", "rf_cfm_loss")
+           "rf_midpoint_half", "rf_interpolant", "rf_cfm_loss", "flow_insert_frames",
+           "flow_frame_schedule")
 
 
 class DitError(RuntimeError):
@@ -78,6 +79,10 @@ def lib() -> ctypes.CDLL:
         for name in ("rf_midpoint_half", "rf_interpolant"):
             getattr(L, name).restype = ctypes.c_int
             getattr(L, name).argtypes = [vp, vp, vp, vp, i64, i32, i64, i32, vp]
+        L.flow_insert_frames.restype = ctypes.c_int
+        L.flow_insert_frames.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i32, i32, i32, vp]
+        L.flow_frame_schedule.restype = ctypes.c_int
+        L.flow_frame_schedule.argtypes = [vp, vp, i64, f32, vp]
         L.rf_cfm_loss.restype = ctypes.c_int
         L.rf_cfm_loss.argtypes = [vp, vp, vp, vp, vp, i64, i32, i64, i32, vp]
         _lib = L
@@ -290,3 +295,41 @@ def rf_cfm_loss(loss_tokens, loss_rows, u, x0, x1, tokens_per_row: int, stream=N
     _check(lib().rf_cfm_loss(_ptr(loss_tokens), _ptr(loss_rows), _ptr(u), _ptr(x0), _ptr(x1), tokens, ch,
                              int(tokens_per_row), _dtype_code(u), _stream(stream)))
     return loss_tokens, loss_rows
+
+
+def flow_insert_frames(z_out, t_out, cu_out, src_out, z, t_frames, cu_seqlens, counts, noise,
+                       tokens_per_frame: int, stream=None):
+    """Insert counts[f] noise frames right after every existing frame f of the packed
+    batch z ([frames * tokens_per_frame, channels]); see include/dit.h."""
+    torch = _torch()
+    _dev(z_out, t_out, cu_out, src_out, z, t_frames, cu_seqlens, counts, noise)
+    _f32(t_out, t_frames)
+    for t in (cu_out, src_out, cu_seqlens, counts):
+        if t.dtype != torch.int32:
+            raise TypeError("offsets, counts and src_out must be int32")
+    if z.dim() != 2 or z_out.dim() != 2 or z_out.shape[1] != z.shape[1] or z_out.dtype != z.dtype:
+        raise ValueError("z and z_out must be [tokens, channels] of one dtype")
+    tpf = int(tokens_per_frame)
+    frames, frames_out = t_frames.numel(), t_out.numel()
+    if z.shape[0] != frames * tpf or z_out.shape[0] != frames_out * tpf or counts.numel() != frames:
+        raise ValueError("z / z_out rows must be frames * tokens_per_frame and counts [frames]")
+    if src_out.numel() != frames_out or cu_out.numel() != cu_seqlens.numel():
+        raise ValueError("src_out must be [frames_out] and cu_out shaped like cu_seqlens")
+    if noise is not None and (noise.dtype != z.dtype or noise.shape != ((frames_out - frames) * tpf, z.shape[1])):
+        raise ValueError("noise must be [(frames_out - frames) * tokens_per_frame, channels] in z's dtype")
+    _check(lib().flow_insert_frames(_ptr(z_out), _ptr(t_out), _ptr(cu_out), _ptr(src_out), _ptr(z),
+                                    _ptr(t_frames), _ptr(cu_seqlens), cu_seqlens.numel() - 1, _ptr(counts),
+                                    _ptr(noise), frames, frames_out, tpf, z.shape[1], _dtype_code(z),
+                                    _stream(stream)))
+    return z_out, t_out, cu_out, src_out
+
+
+def flow_frame_schedule(dt_out, t_frames, dt_max: float, stream=None):
+    """dt_out = min(dt_max, 1 - t_frames); t_frames += dt_out (in place)."""
+    _dev(dt_out, t_frames)
+    _f32(dt_out, t_frames)
+    if dt_out.shape != t_frames.shape or t_frames.dim() != 1:
+        raise ValueError("dt_out and t_frames must be [frames]")
+    _check(lib().flow_frame_schedule(_ptr(dt_out), _ptr(t_frames), t_frames.numel(), float(dt_max),
+                                     _stream(stream)))
+    return dt_out, t_frames

@@ -367,4 +367,54 @@ int rf_cfm_loss(float* loss_tokens, float* loss_rows, const void* u, const void*
     return launched(dit::launch_cfm_loss(a, dtype == DIT_BF16, (hipStream_t)stream), fn);
 }
 
+int flow_insert_frames(void* z_out, float* t_out, int32_t* cu_out, int32_t* src_out,
+                       const void* z, const float* t_frames, const int32_t* cu_seqlens, int32_t num_seqs,
+                       const int32_t* counts, const void* noise, int64_t frames, int64_t frames_out,
+                       int32_t tokens_per_frame, int32_t channels, int32_t dtype, void* stream) {
+    const char* fn = "flow_insert_frames";
+    if (int rc = check_dtype(dtype, fn)) return rc;
+    if (!z_out || !t_out || !cu_out || !src_out || !z || !t_frames || !cu_seqlens || !counts)
+        return fail(DIT_E_INVAL, "%s: NULL pointer argument", fn);
+    if (frames <= 0 || frames_out < frames)
+        return fail(DIT_E_INVAL, "%s: need frames > 0 and frames_out >= frames (got %lld, %lld)", fn,
+                    (long long)frames, (long long)frames_out);
+    if (frames_out > frames && !noise) return fail(DIT_E_INVAL, "%s: noise is NULL but frames are inserted", fn);
+    if (num_seqs <= 0) return fail(DIT_E_INVAL, "%s: num_seqs must be > 0", fn);
+    if (tokens_per_frame <= 0 || channels <= 0) return fail(DIT_E_INVAL, "%s: sizes must be > 0", fn);
+    if (channels % 8 != 0)
+        return fail(DIT_E_UNSUPPORTED, "%s: channels (%d) must be a multiple of 8", fn, channels);
+    if (frames_out * tokens_per_frame > INT32_MAX)
+        return fail(DIT_E_UNSUPPORTED, "%s: output token count exceeds int32 offsets", fn);
+    if (!aligned16(z_out) || !aligned16(z) || (noise && !aligned16(noise)))
+        return fail(DIT_E_UNSUPPORTED, "%s: latents must be 16-byte aligned", fn);
+    if (((uintptr_t)t_out | (uintptr_t)cu_out | (uintptr_t)src_out | (uintptr_t)t_frames |
+         (uintptr_t)cu_seqlens | (uintptr_t)counts) % 4 != 0)
+        return fail(DIT_E_UNSUPPORTED, "%s: index and time arrays must be 4-byte aligned", fn);
+    const int64_t row = (int64_t)channels * elem_size(dtype);
+    const int64_t zb = frames * tokens_per_frame * row, ob = frames_out * tokens_per_frame * row;
+    const int64_t nb = (frames_out - frames) * tokens_per_frame * row;
+    if (overlaps(z_out, ob, z, zb) || (noise && overlaps(z_out, ob, noise, nb)) ||
+        overlaps(t_out, frames_out * 4, t_frames, frames * 4) || overlaps(t_out, frames_out * 4, src_out, frames_out * 4) ||
+        overlaps(src_out, frames_out * 4, counts, frames * 4) || overlaps(cu_out, (num_seqs + 1) * 4, cu_seqlens, (num_seqs + 1) * 4) ||
+        overlaps(cu_out, (num_seqs + 1) * 4, src_out, frames_out * 4) || overlaps(cu_out, (num_seqs + 1) * 4, t_out, frames_out * 4))
+        return fail(DIT_E_INVAL, "%s: outputs must not overlap the inputs or each other", fn);
+    if (int rc = check_device(fn)) return rc;
+    dit::InsertArgs a{z_out, t_out, cu_out, src_out, z, t_frames, cu_seqlens, num_seqs, counts, noise,
+                      frames, frames_out, tokens_per_frame, channels};
+    return launched(dit::launch_insert_frames(a, dtype == DIT_BF16, (hipStream_t)stream), fn);
+}
+
+int flow_frame_schedule(float* dt_out, float* t_frames, int64_t frames, float dt_max, void* stream) {
+    const char* fn = "flow_frame_schedule";
+    if (!dt_out || !t_frames) return fail(DIT_E_INVAL, "%s: NULL pointer argument", fn);
+    if (frames <= 0) return fail(DIT_E_INVAL, "%s: frames must be > 0", fn);
+    if (!(dt_max > 0.f) || !std::isfinite(dt_max)) return fail(DIT_E_INVAL, "%s: dt_max must be finite and > 0", fn);
+    if (((uintptr_t)dt_out | (uintptr_t)t_frames) % 4 != 0)
+        return fail(DIT_E_UNSUPPORTED, "%s: arrays must be 4-byte aligned", fn);
+    if (overlaps(dt_out, frames * 4, t_frames, frames * 4))
+        return fail(DIT_E_INVAL, "%s: dt_out must not overlap t_frames", fn);
+    if (int rc = check_device(fn)) return rc;
+    return launched(dit::launch_frame_schedule(dt_out, t_frames, frames, dt_max, (hipStream_t)stream), fn);
+}
+
 }  // extern "C"

@@ -73,4 +73,14 @@ struct CfmArgs {
 };
 hipError_t launch_cfm_loss(const CfmArgs& a, bool bf16, hipStream_t s);
 
+// Flowception frame insertion (frames of tokens_per_frame token rows)
+struct InsertArgs {
+    void* z_out; float* t_out; int32_t* cu_out; int32_t* src_out;
+    const void* z; const float* t_frames; const int32_t* cu_seqlens; int num_seqs;
+    const int32_t* counts; const void* noise;
+    int64_t frames, frames_out; int tokens_per_frame; int channels;
+};
+hipError_t launch_insert_frames(const InsertArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_frame_schedule(float* dt_out, float* t, int64_t frames, float dt_max, hipStream_t s);
+
 }  // namespace dit

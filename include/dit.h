@@ -12,12 +12,16 @@
  *   rf_midpoint_half     z_mid = z + (dt/2) * u                      (midpoint sampler, stage 1)
  *   rf_interpolant       x_t = (1 - t) x0 + t x1                     (straight-path input)
  *   rf_cfm_loss          |u - (x1 - x0)|^2 per token and per row     (flow-matching loss)
+ *   flow_insert_frames   new noise frames after existing ones        (Flowception insertion)
+ *   flow_frame_schedule  dt_f = min(dt_max, 1 - t_f), t_f += dt_f    (per-frame local times)
  *
  * Definitions come from the pages "DiT, Flow Matching e 3D Attention: A Engenharia
  * de Video com IA" (sections "A ruptura da U-Net", "Flow Matching e Rectified Flow",
  * "3D-RoPE e atencao espaco-temporal", "Engenharia de inferencia e paralelismo de
  * contexto: Ulysses, Ring Attention e FP8") and "Por que e absurdamente dificil
- * gerar um filme inteiro usando IA" (section "Matematica por tras").
+ * gerar um filme inteiro usando IA" (section "Matematica por tras"), and the summary
+ * of "Flowception: Temporally Expansive Flow Matching for Video Generation"
+ * (section 2, "Metodologia: Flowception").
  *
  * Layout (every activation tensor is token-major and contiguous):
  *   hidden x, y, branch      [tokens][d_model]
@@ -256,6 +260,46 @@ int rf_interpolant(void* x_t, const void* x0, const void* x1, const float* t_row
  */
 int rf_cfm_loss(float* loss_tokens, float* loss_rows, const void* u, const void* x0, const void* x1,
                 int64_t tokens, int32_t channels, int64_t tokens_per_row, int32_t dtype, void* stream);
+
+/*
+ * Flowception frame insertion ("Flowception: Temporally Expansive Flow Matching
+ * for Video Generation", technical summary, section 2): during sampling, new
+ * frames are inserted between existing ones, each starting as unit Gaussian
+ * noise with its local time reset to 0. counts[f] new frames go right after
+ * existing frame f (the draw from the predicted insertion rates is the
+ * caller's; passive frames carry 0), taking the noise frames in order.
+ *
+ *   z             [frames * tokens_per_frame][channels] (dtype): the packed batch
+ *   t_frames      [frames] float32 local times
+ *   cu_seqlens    device int32 [num_seqs+1] token offsets of the sequences
+ *                 (multiples of tokens_per_frame, from 0 to frames*tokens_per_frame)
+ *   counts        device int32 [frames], >= 0, summing to frames_out - frames
+ *   noise         [(frames_out - frames) * tokens_per_frame][channels] (dtype);
+ *                 may be NULL when frames_out == frames
+ *   z_out         [frames_out * tokens_per_frame][channels] (dtype)
+ *   t_out         [frames_out] float32: source frames keep their time, new ones 0
+ *   cu_out        device int32 [num_seqs+1]: the new token offsets
+ *   src_out       device int32 [frames_out]: existing frame index, or -1 - n for
+ *                 the n-th noise frame
+ * The device-side arrays (cu_seqlens, counts) are preconditions the host cannot
+ * check; if the counts do not sum to frames_out - frames the call still stays in
+ * bounds (uncovered output frames are zero with src_out = INT32_MIN). No output
+ * may overlap an input or another output; channels % 8 == 0.
+ */
+int flow_insert_frames(void* z_out, float* t_out, int32_t* cu_out, int32_t* src_out,
+                       const void* z, const float* t_frames, const int32_t* cu_seqlens, int32_t num_seqs,
+                       const int32_t* counts, const void* noise, int64_t frames, int64_t frames_out,
+                       int32_t tokens_per_frame, int32_t channels, int32_t dtype, void* stream);
+
+/*
+ * Per-frame schedule of local times (same section): every frame advances from
+ * its own local time, dt_out[f] = min(dt_max, 1 - t_frames[f]) and
+ * t_frames[f] += dt_out[f] in place, so no frame passes t = 1 and a clipped
+ * step lands on exactly 1. dt_out feeds rf_euler_step / rf_midpoint_half with
+ * tokens_per_row = tokens_per_frame.
+ *   dt_out, t_frames  [frames] float32, not overlapping; dt_max > 0
+ */
+int flow_frame_schedule(float* dt_out, float* t_frames, int64_t frames, float dt_max, void* stream);
 
 #ifdef __cplusplus
 }

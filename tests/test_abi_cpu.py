@@ -160,6 +160,32 @@ def test_flow_validation():
     assert L.rf_cfm_loss(FAKE * 12, FAKE * 12, FAKE, FAKE * 4, FAKE * 8, 32, 64, 32, 1, None) == dit.DIT_E_INVAL
 
 
+def test_flowception_validation():
+    L = ensure_built()
+    zo, to, co, so = FAKE * 64, FAKE * 80, FAKE * 81, FAKE * 82
+    z, t, cu, c, nz = FAKE, FAKE * 96, FAKE * 97, FAKE * 98, FAKE * 112
+
+    def call(**kw):
+        a = dict(zo=zo, to=to, co=co, so=so, z=z, t=t, cu=cu, ns=2, c=c, nz=nz, f=10, fo=14, tpf=16, ch=64,
+                 dtype=1)
+        a.update(kw)
+        return L.flow_insert_frames(a["zo"], a["to"], a["co"], a["so"], a["z"], a["t"], a["cu"], a["ns"], a["c"],
+                                    a["nz"], a["f"], a["fo"], a["tpf"], a["ch"], a["dtype"], None)
+    assert call(c=None) == dit.DIT_E_INVAL
+    assert call(fo=9) == dit.DIT_E_INVAL and "frames_out" in _err()
+    assert call(nz=None) == dit.DIT_E_INVAL and "noise" in _err()
+    assert call(ch=12) == dit.DIT_E_UNSUPPORTED
+    assert call(tpf=0) == dit.DIT_E_INVAL
+    assert call(fo=1 << 30) == dit.DIT_E_UNSUPPORTED and "int32" in _err()
+    assert call(zo=z + 64) == dit.DIT_E_INVAL and "overlap" in _err()
+    assert call(to=t) == dit.DIT_E_INVAL
+    assert call(t=FAKE * 96 + 2) == dit.DIT_E_UNSUPPORTED
+    assert L.flow_frame_schedule(None, FAKE, 8, 1.0 / 30, None) == dit.DIT_E_INVAL
+    assert L.flow_frame_schedule(FAKE, FAKE * 2, 0, 1.0 / 30, None) == dit.DIT_E_INVAL
+    assert L.flow_frame_schedule(FAKE, FAKE * 2, 8, 0.0, None) == dit.DIT_E_INVAL
+    assert L.flow_frame_schedule(FAKE, FAKE + 8, 8, 0.1, None) == dit.DIT_E_INVAL and "overlap" in _err()
+
+
 def test_error_text_is_thread_local_and_cleared_on_new_error():
     L = ensure_built()
     L.rf_euler_step(None, None, None, None, 0, 0, 0, 1, None)
