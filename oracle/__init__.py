@@ -27,6 +27,11 @@ What it follows (pages are cited by title and section):
                  Rectified Flow" (x_t = (1 - t) x_0 + t x_1, v = x_1 - x_0),
                  with the interpolant, the flow-matching loss and the midpoint
                  sampler's half step from the same section.
+  * fp8       -- OCP E4M3 encode/decode and per-head quantisation of q, k, v
+                 for FP8 attention: "DiT, Flow Matching e 3D Attention",
+                 section "Engenharia de inferência e paralelismo de contexto:
+                 Ulysses, Ring Attention e FP8" (the attention itself is the
+                 attention oracle on the dequantised values).
   * flowception -- frame insertion with local-time reset and the per-frame
                  schedule: "Flowception: Temporally Expansive Flow Matching for
                  Video Generation", technical summary, section 2.
@@ -35,4 +40,4 @@ Every function is pinned by tests in tests/test_oracle_*.py against closed
 forms, invariants, library special cases or brute force; none is "parity
 unpinned".
 """
-from . import attention, epilogue, flowception, grid, modulate, rope  # noqa: F401
+from . import attention, epilogue, flowception, fp8, grid, modulate, rope  # noqa: F401

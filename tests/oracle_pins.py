@@ -22,6 +22,7 @@ import oracle
 from oracle import attention as o_attn
 from oracle import epilogue as o_epi
 from oracle import flowception as o_flow
+from oracle import fp8 as o_fp8
 from oracle import grid as o_grid
 from oracle import modulate as o_mod
 from oracle import rope as o_rope
@@ -41,6 +42,7 @@ def real_impl():
         interpolant=o_epi.interpolant, velocity=o_epi.velocity,
         interpolant_rows=o_epi.interpolant_rows, cfm_loss=o_epi.cfm_loss, midpoint_half=o_epi.midpoint_half,
         insert_frames=o_flow.insert_frames, frame_schedule=o_flow.frame_schedule,
+        e4m3_encode=o_fp8.e4m3_encode, e4m3_decode=o_fp8.e4m3_decode, quantize_per_head=o_fp8.quantize_per_head,
     )
 
 
@@ -652,6 +654,73 @@ def pin_schedule(impl):
     for _ in range(40):
         _, t = impl.frame_schedule(t, 1.0 / 30)
     assert np.all(t == 1.0)
+
+
+# ------------------------------------------------ FP8 (OCP E4M3)
+def pin_e4m3_spec_values(impl):
+    """Landmarks of the OCP E4M3 format: 1 = 0x38, -2 = 0xC0, the largest
+    finite value 448 = 0x7E, 240 = 0x77, the smallest normal 2^-6 = 0x08, the
+    smallest subnormal 2^-9 = 0x01, 0x7F / 0xFF are NaN."""
+    pairs = {1.0: 0x38, -2.0: 0xC0, 448.0: 0x7E, 240.0: 0x77, 2.0 ** -6: 0x08, 2.0 ** -9: 0x01, 0.0: 0x00}
+    for v, c in pairs.items():
+        assert int(impl.e4m3_encode(np.array([v], np.float32))[0]) == c, (v, hex(c))
+        assert impl.e4m3_decode(np.array([c], np.uint8))[0] == v
+    assert np.all(np.isnan(impl.e4m3_decode(np.array([0x7F, 0xFF], np.uint8))))
+
+
+def pin_e4m3_roundtrip(impl):
+    """Every finite code decodes to a value that encodes back to that code."""
+    c = np.array([i for i in range(256) if i not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(impl.e4m3_encode(impl.e4m3_decode(c).astype(np.float32)), c)
+
+
+def pin_e4m3_nearest_ties_even(impl):
+    """Random values and exact midpoints against a search over all finite
+    codes: the nearest value, ties to the code with an even mantissa."""
+    vals = np.array(sorted({float(v) for v in o_fp8_values()}))
+    r = _rng(70)
+    xs = list(r.uniform(-448, 448, 300)) + list(r.uniform(-0.05, 0.05, 300))
+    xs += [(vals[i] + vals[i + 1]) / 2 for i in range(len(vals) - 1)]   # midpoints
+    xs = np.array(xs, dtype=np.float32)
+    got = impl.e4m3_encode(xs)
+    for x, c in zip(xs, got):
+        d = np.abs(vals - float(x))
+        best = vals[d == d.min()]
+        if len(best) > 1:   # tie: the even mantissa
+            best = [b for b in best if int(impl.e4m3_encode(np.array([b], np.float32))[0]) % 2 == 0]
+        want = abs(best[0]) if x >= 0 else -abs(best[0])
+        if want == 0.0 and np.signbit(x):
+            want = -0.0
+        assert impl.e4m3_decode(np.array([c], np.uint8))[0] == want, (float(x), hex(int(c)))
+
+
+def o_fp8_values():
+    """All finite E4M3 values, listed from the format's definition (sign,
+    exponent with bias 7, 3-bit mantissa; subnormals at exponent 0)."""
+    out = []
+    for e in range(16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue
+            v = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+            out += [v, -v]
+    return out
+
+
+def pin_quantize_per_head(impl):
+    """Each head's largest magnitude maps to +-448 (0x7E / 0xFE); every value is
+    within half a code spacing (relative 2^-4) of its dequantised value; an
+    all-zero head stays zero with scale 1."""
+    r = _rng(71)
+    x = r.standard_normal((40, 3, 16)).astype(np.float32) * np.array([1.0, 30.0, 0.0], np.float32)[None, :, None]
+    codes, amax, scale = impl.quantize_per_head(x)
+    for h in range(2):
+        i = np.unravel_index(np.argmax(np.abs(x[:, h, :])), x[:, h, :].shape)
+        assert codes[i[0], h, i[1]] in (0x7E, 0xFE)
+        deq = impl.e4m3_decode(codes[:, h, :]) * float(scale[h])
+        assert np.all(np.abs(deq - x[:, h, :]) <= np.maximum(np.abs(x[:, h, :]) * 2.0 ** -4, 2.0 ** -10 * scale[h]) * (1 + 1e-6))
+        assert amax[h] == np.abs(x[:, h, :]).max()
+    assert np.all(codes[:, 2, :] == 0) and scale[2] == 1.0
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

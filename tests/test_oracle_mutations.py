@@ -163,6 +163,33 @@ def _schedule_no_clip(t, dt_max):
     return dt, t + dt
 
 
+def _e4m3_truncate(x):
+    """Rounds magnitudes toward zero instead of to nearest."""
+    from oracle import fp8
+    x = np.asarray(x, np.float64)
+    vals = np.array(sorted({abs(float(v)) for v in fp8.e4m3_decode(np.arange(127, dtype=np.uint8)) if not np.isnan(v)}))
+    a = np.abs(x)
+    idx = np.searchsorted(vals, a, side="right") - 1
+    return fp8.e4m3_encode(np.copysign(vals[idx], x).astype(np.float32))
+
+
+def _e4m3_decode_bias8(codes):
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    s = np.where(c >> 7, -1.0, 1.0)
+    e, m = (c >> 3) & 15, c & 7
+    return s * np.where(e == 0, m * 2.0 ** -10, (1 + m / 8) * np.exp2(e - 8.0))
+
+
+def _quantize_per_tensor(x):
+    from oracle import fp8
+    x = np.asarray(x, np.float32)
+    amax = np.float32(np.abs(x).max())
+    inv = np.float32(448.0) / amax
+    codes = fp8.e4m3_encode(np.clip((x * inv).astype(np.float32), -448, 448))
+    h = x.shape[1]
+    return codes, np.full(h, amax, np.float32), np.full(h, amax / np.float32(448), np.float32)
+
+
 def _coords_swapped(n, gh, gw):
     n = np.asarray(n, dtype=np.int64)
     return np.stack([n // (gh * gw), n % gw, (n // gw) % gh], axis=-1)
@@ -218,6 +245,9 @@ MUTANTS = {
     "insert_before_frame": dict(insert_frames=_insert_before),
     "insert_keeps_time": dict(insert_frames=_insert_keep_time),
     "schedule_overshoots": dict(frame_schedule=_schedule_no_clip),
+    "e4m3_truncating": dict(e4m3_encode=_e4m3_truncate),
+    "e4m3_bias_8": dict(e4m3_decode=_e4m3_decode_bias8),
+    "fp8_scale_per_tensor": dict(quantize_per_head=_quantize_per_tensor),
     "grid_h_w_swapped": dict(coords=_coords_swapped),
     "interpolant_reversed": dict(interpolant=_interp_reversed),
     "euler_wrong_sign": dict(euler_step=_euler_minus),
