@@ -29,7 +29,7 @@ DIT_OK, DIT_E_INVAL, DIT_E_UNSUPPORTED, DIT_E_HIP = 0, 1, 2, 3
 EXPORTS = ("dit_last_error", "dit_version", "dit_adaln_modulate", "dit_rope3d",
            "dit_attn3d", "dit_attn3d_lse", "dit_attn_merge", "dit_gated_residual", "rf_euler_step",
            "rf_midpoint_half", "rf_interpolant", "rf_cfm_loss", "flow_insert_frames",
-           "flow_frame_schedule")
+           "flow_frame_schedule", "dit_fp8_v_stride", "dit_quant_fp8", "dit_attn3d_fp8")
 
 
 class DitError(RuntimeError):
@@ -79,6 +79,12 @@ def lib() -> ctypes.CDLL:
         for name in ("rf_midpoint_half", "rf_interpolant"):
             getattr(L, name).restype = ctypes.c_int
             getattr(L, name).argtypes = [vp, vp, vp, vp, i64, i32, i64, i32, vp]
+        L.dit_fp8_v_stride.restype = ctypes.c_int64
+        L.dit_fp8_v_stride.argtypes = [i64, i32]
+        L.dit_quant_fp8.restype = ctypes.c_int
+        L.dit_quant_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, vp, i32, i32, i64, i32, vp]
+        L.dit_attn3d_fp8.restype = ctypes.c_int
+        L.dit_attn3d_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, i32, i32, i64, vp]
         L.flow_insert_frames.restype = ctypes.c_int
         L.flow_insert_frames.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i32, i32, i32, vp]
         L.flow_frame_schedule.restype = ctypes.c_int
@@ -333,3 +339,45 @@ def flow_frame_schedule(dt_out, t_frames, dt_max: float, stream=None):
     _check(lib().flow_frame_schedule(_ptr(dt_out), _ptr(t_frames), t_frames.numel(), float(dt_max),
                                      _stream(stream)))
     return dt_out, t_frames
+
+
+def dit_fp8_v_stride(tokens: int, num_seqs: int) -> int:
+    """Bytes per row of the transposed 8-bit V (see dit_quant_fp8)."""
+    return int(lib().dit_fp8_v_stride(int(tokens), int(num_seqs)))
+
+
+def dit_quant_fp8(q8, k8, v8t, amax, q, k, v, cu_seqlens=None, num_seqs: int = 1, max_seqlen: int = 0,
+                  stream=None):
+    """q, k, v (bf16 [tokens, heads, 128]) -> E4M3 codes q8, k8 (uint8, same shape),
+    v8t (uint8 [heads, 128, v_stride]) and amax (float32 [3, heads])."""
+    torch = _torch()
+    _dev(q8, k8, v8t, amax, q, k, v, cu_seqlens)
+    _f32(amax)
+    if any(t.dtype != torch.uint8 for t in (q8, k8, v8t)):
+        raise TypeError("q8, k8 and v8t must be uint8")
+    if q.dim() != 3 or any(t.shape != q.shape for t in (k, v, q8, k8)) or q.dtype != torch.bfloat16:
+        raise ValueError("q, k, v must be bf16 [tokens, heads, head_dim] and q8, k8 of that shape")
+    tokens, heads, hd = q.shape
+    if cu_seqlens is not None:
+        num_seqs = cu_seqlens.numel() - 1
+    if v8t.dim() != 3 or v8t.shape[:2] != (heads, hd) or amax.shape != (3, heads):
+        raise ValueError("v8t must be [heads, head_dim, v_stride] and amax [3, heads]")
+    _check(lib().dit_quant_fp8(_ptr(q8), _ptr(k8), _ptr(v8t), _ptr(amax), _ptr(q), _ptr(k), _ptr(v), tokens,
+                               heads, hd, _ptr(cu_seqlens), int(num_seqs), int(max_seqlen), v8t.shape[2],
+                               _dtype_code(q), _stream(stream)))
+    return q8, k8, v8t, amax
+
+
+def dit_attn3d_fp8(o, q8, k8, v8t, amax, cu_seqlens=None, num_seqs: int = 1, max_seqlen: int = 0, stream=None):
+    """o (bf16 [tokens, heads, 128]) = attention on the E4M3 codes written by dit_quant_fp8."""
+    torch = _torch()
+    _dev(o, q8, k8, v8t, amax, cu_seqlens)
+    _f32(amax)
+    if o.dtype != torch.bfloat16 or o.dim() != 3 or q8.shape != o.shape or k8.shape != o.shape:
+        raise ValueError("o must be bf16 [tokens, heads, head_dim] and q8, k8 of that shape")
+    tokens, heads, hd = o.shape
+    if cu_seqlens is not None:
+        num_seqs = cu_seqlens.numel() - 1
+    _check(lib().dit_attn3d_fp8(_ptr(o), _ptr(q8), _ptr(k8), _ptr(v8t), _ptr(amax), tokens, heads, hd,
+                                _ptr(cu_seqlens), int(num_seqs), int(max_seqlen), v8t.shape[2], _stream(stream)))
+    return o

@@ -30,6 +30,7 @@ HIP_FLAGS = [
 # for masked keys), so IEEE-mode NaN quieting before every max is dropped there.
 FILE_FLAGS = {
     "k_attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "k_attn_fp8.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
 }
 
 

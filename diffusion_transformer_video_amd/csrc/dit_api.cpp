@@ -417,4 +417,86 @@ int flow_frame_schedule(float* dt_out, float* t_frames, int64_t frames, float dt
     return launched(dit::launch_frame_schedule(dt_out, t_frames, frames, dt_max, (hipStream_t)stream), fn);
 }
 
+int64_t dit_fp8_v_stride(int64_t tokens, int32_t num_seqs) {
+    if (tokens <= 0 || num_seqs <= 0) return 0;
+    return (tokens + 64 * (int64_t)num_seqs + 63) / 64 * 64;
+}
+
+namespace {
+
+int fp8_common(const char* fn, int64_t tokens, int32_t heads, int32_t head_dim, const int32_t* cu_seqlens,
+               int32_t num_seqs, int32_t max_seqlen, int64_t v_stride, int32_t* seqlen_out) {
+    if (tokens <= 0) return fail(DIT_E_INVAL, "%s: tokens must be > 0", fn);
+    if (heads <= 0) return fail(DIT_E_INVAL, "%s: heads must be > 0", fn);
+    if (num_seqs <= 0) return fail(DIT_E_INVAL, "%s: num_seqs must be > 0", fn);
+    if (head_dim != 128) return fail(DIT_E_UNSUPPORTED, "%s: head_dim must be 128 (got %d)", fn, head_dim);
+    int32_t seqlen = max_seqlen;
+    if (cu_seqlens == nullptr) {
+        if (tokens % num_seqs != 0)
+            return fail(DIT_E_INVAL, "%s: dense tokens (%lld) must be a multiple of num_seqs (%d)", fn,
+                        (long long)tokens, num_seqs);
+        if (tokens / num_seqs > 0x7fffffff) return fail(DIT_E_UNSUPPORTED, "%s: sequence too long", fn);
+        seqlen = (int32_t)(tokens / num_seqs);
+    } else if (max_seqlen <= 0 || max_seqlen > tokens) {
+        return fail(DIT_E_INVAL, "%s: packed mode needs 0 < max_seqlen <= tokens (got %d)", fn, max_seqlen);
+    }
+    if (v_stride < dit_fp8_v_stride(tokens, num_seqs) || v_stride % 64 != 0)
+        return fail(DIT_E_INVAL, "%s: v_stride (%lld) must be a multiple of 64 and >= %lld", fn, (long long)v_stride,
+                    (long long)dit_fp8_v_stride(tokens, num_seqs));
+    if ((int64_t)seqlen * heads * head_dim > INT32_MAX || (int64_t)head_dim * v_stride > INT32_MAX)
+        return fail(DIT_E_UNSUPPORTED, "%s: sizes exceed 32-bit offsets", fn);
+    *seqlen_out = seqlen;
+    return DIT_OK;
+}
+
+}  // namespace
+
+int dit_quant_fp8(void* q8, void* k8, void* v8t, float* amax, const void* q, const void* k, const void* v,
+                  int64_t tokens, int32_t heads, int32_t head_dim, const int32_t* cu_seqlens, int32_t num_seqs,
+                  int32_t max_seqlen, int64_t v_stride, int32_t dtype, void* stream) {
+    const char* fn = "dit_quant_fp8";
+    if (int rc = check_dtype(dtype, fn)) return rc;
+    if (dtype != DIT_BF16) return fail(DIT_E_UNSUPPORTED, "%s: inputs must be bf16", fn);
+    if (!q8 || !k8 || !v8t || !amax || !q || !k || !v) return fail(DIT_E_INVAL, "%s: NULL pointer argument", fn);
+    int32_t seqlen = 0;
+    if (int rc = fp8_common(fn, tokens, heads, head_dim, cu_seqlens, num_seqs, max_seqlen, v_stride, &seqlen))
+        return rc;
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+        ((uintptr_t)amax % 4) != 0)
+        return fail(DIT_E_UNSUPPORTED, "%s: tensors must be 16-byte aligned (amax 4-byte)", fn);
+    const int64_t nb = tokens * heads * head_dim, ib = nb * 2, vb = (int64_t)heads * head_dim * v_stride;
+    const int64_t ab = 3 * (int64_t)heads * 4;
+    const void* ins[3] = {q, k, v};
+    void* outs[4] = {q8, k8, v8t, amax};
+    const int64_t osz[4] = {nb, nb, vb, ab};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 3; ++j)
+            if (overlaps(outs[i], osz[i], ins[j], ib)) return fail(DIT_E_INVAL, "%s: outputs must not overlap the inputs", fn);
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], osz[i], outs[j], osz[j])) return fail(DIT_E_INVAL, "%s: outputs must not overlap", fn);
+    }
+    if (int rc = check_device(fn)) return rc;
+    dit::QuantFp8Args a{q8, k8, v8t, amax, q, k, v, tokens, heads, cu_seqlens, num_seqs, seqlen, v_stride};
+    return launched(dit::launch_quant_fp8(a, (hipStream_t)stream), fn);
+}
+
+int dit_attn3d_fp8(void* o, const void* q8, const void* k8, const void* v8t, const float* amax, int64_t tokens,
+                   int32_t heads, int32_t head_dim, const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                   int64_t v_stride, void* stream) {
+    const char* fn = "dit_attn3d_fp8";
+    if (!o || !q8 || !k8 || !v8t || !amax) return fail(DIT_E_INVAL, "%s: NULL pointer argument", fn);
+    int32_t seqlen = 0;
+    if (int rc = fp8_common(fn, tokens, heads, head_dim, cu_seqlens, num_seqs, max_seqlen, v_stride, &seqlen))
+        return rc;
+    if (!aligned16(o) || !aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || ((uintptr_t)amax % 4) != 0)
+        return fail(DIT_E_UNSUPPORTED, "%s: tensors must be 16-byte aligned (amax 4-byte)", fn);
+    const int64_t nb = tokens * heads * head_dim, vb = (int64_t)heads * head_dim * v_stride;
+    if (overlaps(o, nb * 2, q8, nb) || overlaps(o, nb * 2, k8, nb) || overlaps(o, nb * 2, v8t, vb) ||
+        overlaps(o, nb * 2, amax, 3 * (int64_t)heads * 4))
+        return fail(DIT_E_INVAL, "%s: o must not overlap the inputs", fn);
+    if (int rc = check_device(fn)) return rc;
+    dit::AttnFp8Args a{o, q8, k8, v8t, amax, tokens, heads, cu_seqlens, num_seqs, seqlen, v_stride};
+    return launched(dit::launch_attn3d_fp8(a, (hipStream_t)stream), fn);
+}
+
 }  // extern "C"

@@ -1,0 +1,162 @@
+// Pieces shared by the gfx950 attention kernels (bf16 and fp8): lane-pair
+// reductions over the two halves of a wave, buffer loads, the direct HBM -> LDS
+// load, and the block -> (head, sequence, query tile) decode.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+namespace attn {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Max / sum of x over the lane pair (l, l ^ 32): v_permlane32_swap exchanges the
+// upper half of the first operand with the lower half of the second, so with
+// both operands = x the two results hold (own, partner) in some order per lane.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource (raw, 32-bit range checked) for `bytes` bytes at `p`.
+__device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const i32x4 r = {(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+    return r;
+}
+
+// One wave-wide 16-byte-per-lane load HBM -> LDS: lane L's 16 bytes land at
+// lds_addr + 16 L. Issued from inline asm so that the compiler does not treat
+// the pending load as a possible writer of the LDS tiles being read meanwhile
+// (it would then wait for it before every LDS read); completion is waited for
+// explicitly (vmcnt) before the barrier that publishes the tile. M0 is saved and
+// restored around the instruction. The asm has no register outputs.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(lds_ptr_t)(const_cast<void*>(p));   // LDS byte address
+}
+
+// Materialise v here, with every lane active. A matrix-core product reads its
+// operands only from the active lanes, and the compiler is free to sink the last
+// products of the key loop into the lane-divergent branch of the store that
+// alone consumes them (rows past the sequence end are inactive there), which
+// would silently drop the inactive lanes' rows of V and columns of P. The empty
+// asm consumes and redefines v outside that branch; it emits no instruction.
+template <typename T>
+__device__ __forceinline__ void pin_all_lanes(T& v) {
+    asm volatile("" : "+v"(v));
+}
+
+// Work item of one block: query tile qt of sequence seq, head head; the
+// sequence's queries start at row s0 (len of them), its keys at row k0 (klen).
+struct BlockWork {
+    int head, seq, qt;
+    int64_t s0, k0;
+    int len, klen;
+};
+
+// Work items are numbered head-major over the exact query tiles (BQ queries) of
+// every sequence (longest sequence first within a head) and remapped so that
+// each XCD -- the dispatcher deals blocks round-robin over the 8 XCDs, so an
+// XCD receives a contiguous range of items -- gets whole heads with all their
+// sequences (balanced), and its concurrent blocks share one head's K/V in L2.
+// Blocks past the real total (the grid is sized for num_seqs x the longest
+// sequence) are dealt last and get false. cu_q NULL: dense sequences of max_q
+// queries and max_k keys. Every decoded value is wave-uniform.
+__device__ __forceinline__ bool decode_block(const int32_t* cu_q, const int32_t* cu_k, int num_seqs, int max_q,
+                                             int max_k, int heads, int nqt, int BQ, BlockWork& w) {
+    int total, seq, qt, head;
+    int64_t s0, k0;   // first query row / first key row of the sequence
+    int len, klen;    // its queries / keys
+    if (cu_q == nullptr) {
+        total = (int)gridDim.x;
+    } else {
+        total = 0;
+        for (int s = 0; s < num_seqs; ++s) {
+            const int ls = __builtin_amdgcn_readfirstlane(cu_q[s + 1] - cu_q[s]);
+            total += (ls + BQ - 1) / BQ;
+        }
+        total *= heads;
+    }
+    const int b = (int)blockIdx.x;
+    if (b >= total) return false;
+    {
+        const int per = total / 8, rem = total % 8;
+        const int xcd = b % 8, idx = b / 8;
+        const int w = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+        if (cu_q == nullptr) {
+            const int per_head = nqt * num_seqs;
+            head = __builtin_amdgcn_readfirstlane(w / per_head);
+            const int r = w - head * per_head;
+            seq = __builtin_amdgcn_readfirstlane(r / nqt);
+            qt = __builtin_amdgcn_readfirstlane(r - seq * nqt);
+            s0 = (int64_t)seq * max_q;
+            len = max_q;
+            k0 = (int64_t)seq * max_k;
+            klen = max_k;
+        } else {
+            const int per_head = total / heads;
+            head = __builtin_amdgcn_readfirstlane(w / per_head);
+            int r = __builtin_amdgcn_readfirstlane(w - head * per_head);
+            // walk the sequences longest first (by queries; ties: lower index first);
+            // num_seqs is small, so the O(n^2) rank walk is a handful of scalar steps
+            seq = -1;
+            int prev_len = 0x7fffffff, prev_idx = -1;
+            for (int k = 0; k < num_seqs && seq < 0; ++k) {
+                // next sequence in (length desc, index asc) order after (prev_len, prev_idx)
+                int best = -1, best_len = -1;
+                for (int s = 0; s < num_seqs; ++s) {
+                    const int ls = __builtin_amdgcn_readfirstlane(cu_q[s + 1] - cu_q[s]);
+                    const bool after = num_seqs > 32 ? s > prev_idx   // many sequences: index order
+                                                       : ls < prev_len || (ls == prev_len && s > prev_idx);
+                    if (after && (num_seqs > 32 ? best < 0 : ls > best_len)) { best = s; best_len = ls; }
+                }
+                const int nt = (best_len + BQ - 1) / BQ;
+                if (r < nt) { seq = best; qt = r; } else { r -= nt; prev_len = best_len; prev_idx = best; }
+            }
+            seq = __builtin_amdgcn_readfirstlane(seq);
+            qt = __builtin_amdgcn_readfirstlane(qt);
+            const int c0 = __builtin_amdgcn_readfirstlane(cu_q[seq]);
+            const int c1 = __builtin_amdgcn_readfirstlane(cu_q[seq + 1]);
+            s0 = c0;
+            len = c1 - c0;
+            const int d0 = __builtin_amdgcn_readfirstlane(cu_k[seq]);
+            const int d1 = __builtin_amdgcn_readfirstlane(cu_k[seq + 1]);
+            k0 = d0;
+            klen = d1 - d0;
+        }
+    }
+    w.head = head;
+    w.seq = seq;
+    w.qt = qt;
+    w.s0 = s0;
+    w.k0 = k0;
+    w.len = len;
+    w.klen = klen;
+    return true;
+}
+
+}  // namespace attn
+}  // namespace dit

@@ -83,4 +83,23 @@ struct InsertArgs {
 hipError_t launch_insert_frames(const InsertArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_frame_schedule(float* dt_out, float* t, int64_t frames, float dt_max, hipStream_t s);
 
+// FP8 (OCP E4M3) attention, head_dim 128: quantisation of bf16 q, k, v and the
+// attention on the codes (layouts in k_quant_fp8.hip)
+struct QuantFp8Args {
+    void* q8; void* k8; void* v8t; float* amax;   // amax [3][heads]: q, k, v
+    const void* q; const void* k; const void* v;
+    int64_t tokens; int heads;
+    const int32_t* cu_seqlens; int num_seqs; int max_seqlen;
+    int64_t ldv;   // bytes per v8t row
+};
+hipError_t launch_quant_fp8(const QuantFp8Args& a, hipStream_t s);
+
+struct AttnFp8Args {
+    void* o; const void* q8; const void* k8; const void* v8t; const float* amax;
+    int64_t tokens; int heads;
+    const int32_t* cu_seqlens; int num_seqs; int max_seqlen;
+    int64_t ldv;
+};
+hipError_t launch_attn3d_fp8(const AttnFp8Args& a, hipStream_t s);
+
 }  // namespace dit

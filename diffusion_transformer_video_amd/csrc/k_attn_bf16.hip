@@ -43,17 +43,19 @@
 //     the sequence are clamped on load and never stored.
 #include <math.h>
 
+#include "dit_attn_common.hpp"
 #include "dit_device.hpp"
 #include "dit_internal.h"
 
 namespace dit {
 namespace {
 
+using namespace attn;
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr float kLazyRescale = 8.0f;   // log2 headroom before the max is raised
 
@@ -87,53 +89,6 @@ template <int CPR>
 __device__ __forceinline__ int kswz(int r) { return (r / (16 / CPR)) & (CPR - 1); }
 template <int CPR>
 __device__ __forceinline__ int vswz(int r) { return 4 * ((r / (16 / CPR)) % (CPR / 4)); }
-
-// Max / sum of x over the lane pair (l, l ^ 32): v_permlane32_swap exchanges the
-// upper half of the first operand with the lower half of the second, so with
-// both operands = x the two results hold (own, partner) in some order per lane.
-__device__ __forceinline__ float pair_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer resource (raw, 32-bit range checked) for `bytes` bytes at `p`.
-__device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(p);
-    const i32x4 r = {(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
-    return r;
-}
-
-// One wave-wide 16-byte-per-lane load HBM -> LDS: lane L's 16 bytes land at
-// lds_addr + 16 L. Issued from inline asm so that the compiler does not treat
-// the pending load as a possible writer of the LDS tiles being read meanwhile
-// (it would then wait for it before every LDS read); completion is waited for
-// explicitly (vmcnt) before the barrier that publishes the tile. M0 is saved and
-// restored around the instruction. The asm has no register outputs.
-__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
-        : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(lds_ptr_t)(const_cast<void*>(p));   // LDS byte address
-}
 
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -489,74 +444,13 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     __shared__ __attribute__((aligned(1024))) char kbuf[C::ST][C::TILEB];
     __shared__ __attribute__((aligned(1024))) char vbuf[C::ST][C::TILEB];
 
-    // ---- block -> (head, sequence, query tile)
-    // Work items are numbered head-major over the exact query tiles of every
-    // sequence (longest sequence first within a head), so that each XCD -- which
-    // receives a contiguous range of items -- gets whole heads with all their
-    // sequences (balanced) and its concurrent blocks share one head's K/V in L2.
-    // Blocks past the real total (the grid is sized for num_seqs x the longest
-    // sequence) are dealt last by the dispatcher and exit at once.
-    int total, seq, qt, head;
-    int64_t s0, k0;   // first query row / first key row of the sequence
-    int len, klen;    // its queries / keys
-    if (a.cu_seqlens == nullptr) {
-        total = (int)gridDim.x;
-    } else {
-        total = 0;
-        for (int s = 0; s < a.num_seqs; ++s) {
-            const int ls = __builtin_amdgcn_readfirstlane(a.cu_seqlens[s + 1] - a.cu_seqlens[s]);
-            total += (ls + BQ - 1) / BQ;
-        }
-        total *= a.heads;
-    }
-    const int b = (int)blockIdx.x;
-    if (b >= total) return;
-    {
-        const int per = total / 8, rem = total % 8;
-        const int xcd = b % 8, idx = b / 8;
-        const int w = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-        if (a.cu_seqlens == nullptr) {
-            const int per_head = nqt * a.num_seqs;
-            head = __builtin_amdgcn_readfirstlane(w / per_head);
-            const int r = w - head * per_head;
-            seq = __builtin_amdgcn_readfirstlane(r / nqt);
-            qt = __builtin_amdgcn_readfirstlane(r - seq * nqt);
-            s0 = (int64_t)seq * a.max_seqlen;
-            len = a.max_seqlen;
-            k0 = (int64_t)seq * a.max_seqlen_k;
-            klen = a.max_seqlen_k;
-        } else {
-            const int per_head = total / a.heads;
-            head = __builtin_amdgcn_readfirstlane(w / per_head);
-            int r = __builtin_amdgcn_readfirstlane(w - head * per_head);
-            // walk the sequences longest first (by queries; ties: lower index first);
-            // num_seqs is small, so the O(n^2) rank walk is a handful of scalar steps
-            seq = -1;
-            int prev_len = 0x7fffffff, prev_idx = -1;
-            for (int k = 0; k < a.num_seqs && seq < 0; ++k) {
-                // next sequence in (length desc, index asc) order after (prev_len, prev_idx)
-                int best = -1, best_len = -1;
-                for (int s = 0; s < a.num_seqs; ++s) {
-                    const int ls = __builtin_amdgcn_readfirstlane(a.cu_seqlens[s + 1] - a.cu_seqlens[s]);
-                    const bool after = a.num_seqs > 32 ? s > prev_idx   // many sequences: index order
-                                                       : ls < prev_len || (ls == prev_len && s > prev_idx);
-                    if (after && (a.num_seqs > 32 ? best < 0 : ls > best_len)) { best = s; best_len = ls; }
-                }
-                const int nt = (best_len + BQ - 1) / BQ;
-                if (r < nt) { seq = best; qt = r; } else { r -= nt; prev_len = best_len; prev_idx = best; }
-            }
-            seq = __builtin_amdgcn_readfirstlane(seq);
-            qt = __builtin_amdgcn_readfirstlane(qt);
-            const int c0 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq]);
-            const int c1 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq + 1]);
-            s0 = c0;
-            len = c1 - c0;
-            const int d0 = __builtin_amdgcn_readfirstlane(a.cu_seqlens_k[seq]);
-            const int d1 = __builtin_amdgcn_readfirstlane(a.cu_seqlens_k[seq + 1]);
-            k0 = d0;
-            klen = d1 - d0;
-        }
-    }
+    // ---- block -> (head, sequence, query tile), XCD-aware (decode_block)
+    attn::BlockWork bw;
+    if (!attn::decode_block(a.cu_seqlens, a.cu_seqlens_k, a.num_seqs, a.max_seqlen, a.max_seqlen_k, a.heads, nqt,
+                            BQ, bw))
+        return;
+    const int head = bw.head, qt = bw.qt, len = bw.len, klen = bw.klen;
+    const int64_t s0 = bw.s0, k0 = bw.k0;
     const int q0 = qt * BQ;
     if (q0 >= len) return;
     if (klen == 0) {   // no keys: o = 0, lse = -inf (the empty sum)
@@ -664,6 +558,10 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     for (int j = 0; j + 2 < p.ntiles; ++j) pipe_step<HD, NW, QB, false>(p, j, S, kbuf[0], vbuf[0]);
     if (p.ntiles > 1) pipe_step<HD, NW, QB, true>(p, p.ntiles - 2, S, kbuf[0], vbuf[0]);
     pipe_last<HD, NW, QB>(p, S, lds_addr(vbuf[0]) + ((p.ntiles - 1) % C::ST) * C::TILEB);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) pin_all_lanes(p.O[qb][dt]);
 
     // ---- normalise and store: lane holds query my_q[qb], d = 32dt + 8(r/4) + 4g + r%4;
     // lanes l and l^32 summed disjoint keys of the same query

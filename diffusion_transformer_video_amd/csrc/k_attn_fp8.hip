@@ -1,0 +1,328 @@
+// FP8 (OCP E4M3) attention on gfx950 matrix cores: both products on
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales), fp32 accumulation.
+//
+// o = softmax(q k^T / sqrt(d_head)) v per (sequence, head) on the dequantised
+// values ("Por que e absurdamente dificil gerar um filme inteiro usando IA",
+// section "Matematica por tras"; the 8-bit quantisation of "DiT, Flow Matching e
+// 3D Attention", section "Engenharia de inferencia e paralelismo de contexto:
+// Ulysses, Ring Attention e FP8"). Inputs are the codes and per-head amax values
+// written by the quantisation kernel (k_quant_fp8.hip): dequantisation scales
+// amax / 448 fold into the exponent (q, k) and into the final normalisation (v).
+//
+// Same organisation as the bf16 kernel (8 waves x 32 queries per block, 64-key
+// tiles through 3-deep LDS rings loaded with direct HBM -> LDS loads, one
+// barrier per tile, transposed scores S^T = K Q^T so a lane holds 32 keys of one
+// query), with 8-bit operands:
+//   * one 32x32x64 product consumes 64 head dims (S) or 64 keys (O), so a tile
+//     takes 4 + 4 products per wave instead of 16 + 16, and moves half the LDS
+//     bytes;
+//   * operand bytes pair up by (lane half, byte index) in both A and B (probed),
+//     so lane half h of the scores holds keys {32b + 8q + 4h + i}; V is stored
+//     transposed with exactly those keys at columns 32h + 16b + 4q + i, and
+//     the probabilities go from the score registers into the B operand with
+//     no lane exchange and no transposing read;
+//   * probabilities are exp2(s - m + 6) with the running max m raised whenever
+//     a tile max exceeds it by more than 2: the largest weight lies in
+//     [2^6, 2^8] (E4M3 holds up to 448), so weights down to 2^-12 of the
+//     largest keep E4M3's full 3-bit precision. The row sum adds the unrounded
+//     probabilities.
+#include <math.h>
+
+#include "dit_attn_common.hpp"
+#include "dit_device.hpp"
+#include "dit_internal.h"
+
+namespace dit {
+namespace {
+
+using namespace attn;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+
+constexpr int HD = 128, NW = 8, BK = 64, ST = 3;
+constexpr int BQ = 32 * NW;          // queries per block
+constexpr int TILEB = BK * HD;       // bytes of a K tile (64 rows x 128) or a V^T tile (128 rows x 64)
+constexpr float kLazy = 2.0f;        // log2 headroom before the max is raised
+constexpr float kPOffset = 6.0f;     // exp2 offset of the probabilities
+constexpr float kE4M3Max = 448.0f;
+
+// LDS swizzles of 16-byte chunks: K rows have 8 chunks, V^T rows 4. A 16-lane
+// group of an operand read takes 16 consecutive rows at one logical chunk; the
+// XOR spreads them over all 64 banks.
+__device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int vswz(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ i32x8 lds_op(uint32_t a0, uint32_t a1) {
+    const u32x4 x = *(lds_u32x4*)(uintptr_t)a0;
+    const u32x4 y = *(lds_u32x4*)(uintptr_t)a1;
+    const i32x8 r = {(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+    return r;
+}
+
+__device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);   // e4m3 x e4m3, scale 1
+}
+
+__device__ __forceinline__ float max16(const f32x16& S) {
+    float mx = __builtin_fmaxf(S[0], __builtin_fmaxf(S[1], S[2]));
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(S[r], S[r + 1]));
+    return __builtin_fmaxf(mx, S[15]);
+}
+
+struct State {
+    i32x4 rk, rv;
+    int wave, lane, g, len, ntiles;
+    uint32_t ldk, koff, voff;
+    uint32_t kaddr[4];   // K operand chunk addresses within a tile: (step i, chunk t) -> 2i + t
+    uint32_t vaddr[2];   // V^T operand chunk addresses within a tile, d block 0
+    i32x8 qreg[2];       // Q (B operand of S^T) for head dims 0..63 and 64..127
+    f32x16 O[4];
+    float m_run, l_run, c;
+};
+
+// K tile (keys kbase..kbase+63): wave w moves rows 8w..8w+7 (1 KB); lane L
+// carries row 8w + L/8 at physical chunk L%8.
+__device__ __forceinline__ void issue_k(const State& p, char* dst, uint32_t kbase) {
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(dst) + 1024 * p.wave);
+    if (kbase + BK <= (uint32_t)p.len) {
+        dma16(p.rk, lbase, p.koff, kbase * p.ldk);
+    } else {   // last tile: rows past the end repeat the last row (masked later)
+        const uint32_t r0 = (uint32_t)(8 * p.wave + p.lane / 8);
+        const uint32_t rows_left = (uint32_t)p.len - kbase;
+        const uint32_t r = r0 < rows_left ? r0 : rows_left - 1;
+        dma16(p.rk, lbase, r * p.ldk + (uint32_t)(((p.lane % 8) ^ kswz((int)r0)) * 16), kbase * p.ldk);
+    }
+}
+
+// V^T tile j: wave w moves rows 16w..16w+15 (1 KB); lane L carries row
+// 16w + L/4 at physical chunk L%4. The sequence is padded to whole tiles.
+__device__ __forceinline__ void issue_v(const State& p, char* dst, uint32_t j) {
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(dst) + 1024 * p.wave);
+    dma16(p.rv, lbase, p.voff, 64 * j);
+}
+
+__device__ __forceinline__ void s_tile(const State& p, uint32_t kt, f32x16 (&S)[2]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { S[0][r] = 0.f; S[1][r] = 0.f; }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const uint32_t base = kt + kb * 32 * HD;
+            S[kb] = mfma8(lds_op(base + p.kaddr[2 * i], base + p.kaddr[2 * i + 1]), p.qreg[i], S[kb]);
+        }
+}
+
+__device__ __forceinline__ void mask_tile(f32x16 (&S)[2], int g, int kbase, int len) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int k = kbase + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (k >= len) S[0][r] = -INFINITY;
+        if (k + 32 >= len) S[1][r] = -INFINITY;
+    }
+}
+
+// raise the running max (rescaling O and l) when the tile max exceeds it by more
+// than kLazy -- a wave-uniform branch
+__device__ __forceinline__ void max_update(State& p, const f32x16 (&S)[2]) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(__builtin_fmaxf(max16(S[0]), max16(S[1]))),
+                                                    __float_as_uint(__builtin_fmaxf(max16(S[0]), max16(S[1]))),
+                                                    false, false);
+    const float mxs = __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * p.c;
+    if (__builtin_amdgcn_ballot_w64(mxs > p.m_run + kLazy) != 0) {
+        const float m_new = __builtin_fmaxf(p.m_run, mxs);
+        const float alpha = __builtin_amdgcn_exp2f(p.m_run - m_new);
+        p.l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p.O[dt][r] *= alpha;
+        p.m_run = m_new;
+    }
+}
+
+// probabilities of the tile in S as the B operand of O^T += V^T P^T (byte
+// 16b + r of the lane's 32 = score S[b][r]) and their unrounded row sum
+__device__ __forceinline__ i32x8 probs(State& p, const f32x16 (&S)[2]) {
+    const float off = kPOffset - p.m_run;
+    int w[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * t + e;
+            v[e] = __builtin_amdgcn_exp2f(fmaf(S[j >> 4][j & 15], p.c, off));
+            p.l_run += v[e];
+        }
+        int d = 0;
+        d = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], d, false);
+        d = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], d, true);
+        w[t] = d;
+    }
+    const i32x8 r = {w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
+    return r;
+}
+
+__device__ __forceinline__ void pv_tile(State& p, uint32_t vt, const i32x8& P) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        const uint32_t base = vt + dt * 32 * BK;
+        p.O[dt] = mfma8(lds_op(base + p.vaddr[0], base + p.vaddr[1]), P, p.O[dt]);
+    }
+}
+
+__global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(AttnFp8Args a, int nqt) {
+    __shared__ __attribute__((aligned(1024))) char kbuf[ST][TILEB];
+    __shared__ __attribute__((aligned(1024))) char vbuf[ST][TILEB];
+
+    BlockWork bw;
+    if (!decode_block(a.cu_seqlens, a.cu_seqlens, a.num_seqs, a.max_seqlen, a.max_seqlen, a.heads, nqt, BQ, bw))
+        return;
+    const int head = bw.head, len = bw.len;
+    const int q0 = bw.qt * BQ;
+    if (q0 >= len) return;
+    // first column of the sequence in v8t: sequences padded to whole tiles
+    int64_t pstart;
+    if (a.cu_seqlens == nullptr) {
+        pstart = (int64_t)bw.seq * ((a.max_seqlen + BK - 1) / BK) * BK;
+    } else {
+        pstart = 0;
+        for (int s = 0; s < bw.seq; ++s) {
+            const int ls = __builtin_amdgcn_readfirstlane(a.cu_seqlens[s + 1] - a.cu_seqlens[s]);
+            pstart += (int64_t)((ls + BK - 1) / BK) * BK;
+        }
+    }
+
+    State p;
+    const int tid = threadIdx.x;
+    p.lane = tid & 63;
+    p.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    p.g = p.lane >> 5;
+    const int l32 = p.lane & 31;
+    p.len = len;
+    p.ntiles = (len + BK - 1) / BK;
+    p.ldk = (uint32_t)a.heads * HD;   // token stride of q8 / k8 in bytes
+    const int64_t base = (bw.s0 * a.heads + head) * (int64_t)HD;
+    const uint32_t span = (uint32_t)len * p.ldk;
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<const uint8_t*>(a.q8) + base), (short)0, span,
+                                          0x00020000);
+    p.rk = make_rsrc(reinterpret_cast<const uint8_t*>(a.k8) + base, span);
+    p.rv = make_rsrc(reinterpret_cast<const uint8_t*>(a.v8t) + (int64_t)head * HD * a.ldv + pstart,
+                     (uint32_t)(HD * a.ldv - pstart));
+    {
+        const int kr = 8 * p.wave + p.lane / 8;
+        p.koff = (uint32_t)kr * p.ldk + (uint32_t)(((p.lane % 8) ^ kswz(kr)) * 16);
+        const int vr = 16 * p.wave + p.lane / 4;
+        p.voff = (uint32_t)vr * (uint32_t)a.ldv + (uint32_t)(((p.lane % 4) ^ vswz(vr)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            p.kaddr[2 * i + t] = (uint32_t)(l32 * HD + (((4 * i + 2 * p.g + t) ^ kswz(l32)) * 16));
+#pragma unroll
+    for (int t = 0; t < 2; ++t) p.vaddr[t] = (uint32_t)(l32 * BK + (((2 * p.g + t) ^ vswz(l32)) * 16));
+
+    // ---- Q: lane holds query q0 + 32 wave + l32, head dims 64i + 32g .. +31
+    const int my_q = q0 + 32 * p.wave + l32;
+    {
+        const uint32_t qrow = (uint32_t)(my_q < len ? my_q : len - 1);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint4 x = bload(rq, qrow * p.ldk + 64 * i + 32 * p.g, 0);
+            const uint4 y = bload(rq, qrow * p.ldk + 64 * i + 32 * p.g + 16, 0);
+            const i32x8 r = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+            p.qreg[i] = r;
+        }
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p.O[dt][r] = 0.f;
+    p.m_run = -INFINITY;
+    p.l_run = 0.f;
+    const float sq = a.amax[head] / kE4M3Max, sk = a.amax[a.heads + head] / kE4M3Max;
+    const float sv = a.amax[2 * a.heads + head] / kE4M3Max;
+    // log2(e) / sqrt(128); kept >= the smallest normal float so that a head whose q
+    // or k is all zero (scale 0) gets uniform weights rather than -inf * 0 on the
+    // masked keys (its true scores are all 0; this moves them by < 1e-30)
+    p.c = __builtin_fmaxf(sq * sk * (1.4426950408889634f / 11.313708498984761f), 1.17549435e-38f);
+
+    // ---- prologue: K(0), V(0), K(1) resident; S(0) and its max; then the loads a
+    // step -1 would have issued (K(2), V(1))
+    issue_k(p, kbuf[0], 0);
+    issue_v(p, vbuf[0], 0);
+    if (p.ntiles > 1) issue_k(p, kbuf[1], BK);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    f32x16 S[2];
+    s_tile(p, __builtin_amdgcn_readfirstlane(lds_addr(kbuf[0])), S);
+    if (p.ntiles == 1) mask_tile(S, p.g, 0, len);
+    max_update(p, S);
+    __syncthreads();   // all reads of K(0) done before its slot is refilled
+    if (p.ntiles > 2) issue_k(p, kbuf[2], 2 * BK);
+    if (p.ntiles > 1) issue_v(p, vbuf[1], 1);
+
+    // ---- steady state: step j holds S(j); K(j+1), V(j) resident
+    for (int j = 0; j + 1 < p.ntiles; ++j) {
+        const int kn = j + 3, vn = j + 2;
+        const bool ik = kn < p.ntiles, iv = vn < p.ntiles;
+        if (ik) issue_k(p, kbuf[kn % ST], (uint32_t)kn * BK);
+        if (iv) issue_v(p, vbuf[vn % ST], (uint32_t)vn);
+        const uint32_t kt = __builtin_amdgcn_readfirstlane(lds_addr(kbuf[(j + 1) % ST]));
+        const uint32_t vt = __builtin_amdgcn_readfirstlane(lds_addr(vbuf[j % ST]));
+        const i32x8 P = probs(p, S);
+        s_tile(p, kt, S);   // S(j+1): independent of the probabilities above
+        pv_tile(p, vt, P);
+        if (j + 1 == p.ntiles - 1) mask_tile(S, p.g, (j + 1) * BK, len);
+        max_update(p, S);
+        // the next step reads K(j+2), V(j+1), issued one step earlier; this step's
+        // own loads (completing in issue order) may stay in flight
+        if (ik)
+            asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        else if (iv)
+            asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    {
+        const i32x8 P = probs(p, S);
+        pv_tile(p, __builtin_amdgcn_readfirstlane(lds_addr(vbuf[(p.ntiles - 1) % ST])), P);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) pin_all_lanes(p.O[dt]);
+
+    // ---- normalise and store: lane holds query my_q, d = 32dt + 8(r/4) + 4g + r%4
+    const float inv = sv / pair_sum(p.l_run);   // lanes l and l^32 summed disjoint keys
+    if (my_q < len) {
+        uint2* Og = reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(a.o) + base + (int64_t)my_q * a.heads * HD);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                uint2 wv;
+                wv.x = pack_bf16x2(p.O[dt][4 * rg + 0] * inv, p.O[dt][4 * rg + 1] * inv);
+                wv.y = pack_bf16x2(p.O[dt][4 * rg + 2] * inv, p.O[dt][4 * rg + 3] * inv);
+                Og[(dt * 32 + 8 * rg + 4 * p.g) / 4] = wv;
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn3d_fp8(const AttnFp8Args& a, hipStream_t s) {
+    const int nqt = (a.max_seqlen + BQ - 1) / BQ;
+    const int64_t total = (int64_t)nqt * a.heads * a.num_seqs;
+    if (total <= 0) return hipSuccess;
+    if (total > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_fp8_kernel, dim3((unsigned)total), dim3(64 * NW), 0, s, a, nqt);
+    return hipGetLastError();
+}
+
+}  // namespace dit

@@ -12,6 +12,8 @@
  *   rf_midpoint_half     z_mid = z + (dt/2) * u                      (midpoint sampler, stage 1)
  *   rf_interpolant       x_t = (1 - t) x0 + t x1                     (straight-path input)
  *   rf_cfm_loss          |u - (x1 - x0)|^2 per token and per row     (flow-matching loss)
+ *   dit_quant_fp8        q, k, v -> E4M3 codes + per-head amax       (8-bit attention inputs)
+ *   dit_attn3d_fp8       attention on the E4M3 codes                 (8-bit attention)
  *   flow_insert_frames   new noise frames after existing ones        (Flowception insertion)
  *   flow_frame_schedule  dt_f = min(dt_max, 1 - t_f), t_f += dt_f    (per-frame local times)
  *
@@ -260,6 +262,39 @@ int rf_interpolant(void* x_t, const void* x0, const void* x1, const float* t_row
  */
 int rf_cfm_loss(float* loss_tokens, float* loss_rows, const void* u, const void* x0, const void* x1,
                 int64_t tokens, int32_t channels, int64_t tokens_per_row, int32_t dtype, void* stream);
+
+/*
+ * 8-bit floating point attention ("DiT, Flow Matching e 3D Attention", section
+ * "Engenharia de inferencia e paralelismo de contexto: Ulysses, Ring Attention
+ * e FP8", which pairs FlashAttention-3 with 8-bit quantisation). Format: OCP
+ * E4M3 (bias 7, 3 mantissa bits, max 448, round to nearest even). One scale
+ * per (tensor, head): amax[t][h] = max |x_t[:, h, :]|; codes =
+ * E4M3(clamp(x * (448 / amax), +-448)); dequantised value = code * amax / 448;
+ * an all-zero head has codes 0.
+ *
+ * dit_quant_fp8 writes
+ *   q8, k8     [tokens][heads][128] uint8 codes (row-major like q, k)
+ *   v8t        [heads][128][v_stride] uint8: V transposed for the attention
+ *              kernel -- each sequence padded with zero codes to a multiple of
+ *              64 keys, sequences one after another, and inside each tile of 64
+ *              keys key 32b + 8q + 4h + i at column 32h + 16b + 4q + i
+ *   amax       [3][heads] float32 (q, k, v)
+ * from bf16 q, k, v [tokens][heads][128]. v_stride (bytes per v8t row) must be
+ * a multiple of 64 and >= dit_fp8_v_stride(tokens, num_seqs).
+ *
+ * dit_attn3d_fp8: o (bf16 [tokens][heads][128]) = softmax(q k^T / sqrt(128)) v
+ * over the dequantised values, both products on E4M3 matrix cores with float32
+ * accumulation; the probabilities enter the second product rounded to E4M3.
+ * Sequences as dit_attn3d (dense: cu_seqlens NULL; packed: device offsets and
+ * max_seqlen). head_dim must be 128. Outputs must not overlap inputs.
+ */
+int64_t dit_fp8_v_stride(int64_t tokens, int32_t num_seqs);
+int dit_quant_fp8(void* q8, void* k8, void* v8t, float* amax, const void* q, const void* k, const void* v,
+                  int64_t tokens, int32_t heads, int32_t head_dim, const int32_t* cu_seqlens, int32_t num_seqs,
+                  int32_t max_seqlen, int64_t v_stride, int32_t dtype, void* stream);
+int dit_attn3d_fp8(void* o, const void* q8, const void* k8, const void* v8t, const float* amax, int64_t tokens,
+                   int32_t heads, int32_t head_dim, const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                   int64_t v_stride, void* stream);
 
 /*
  * Flowception frame insertion ("Flowception: Temporally Expansive Flow Matching

@@ -186,6 +186,29 @@ def test_flowception_validation():
     assert L.flow_frame_schedule(FAKE, FAKE + 8, 8, 0.1, None) == dit.DIT_E_INVAL and "overlap" in _err()
 
 
+def test_fp8_validation():
+    L = ensure_built()
+    assert L.dit_fp8_v_stride(100, 2) == 256 and L.dit_fp8_v_stride(0, 1) == 0
+    q8, k8, v8t, am, q, k, v = FAKE * 16, FAKE * 24, FAKE * 32, FAKE * 64, FAKE, FAKE * 4, FAKE * 8
+    vs = L.dit_fp8_v_stride(64, 1)
+
+    def quant(**kw):
+        a = dict(q8=q8, k8=k8, vt=v8t, am=am, q=q, k=k, v=v, t=64, h=2, hd=128, cu=None, ns=1, mx=0, vs=vs, dt=1)
+        a.update(kw)
+        return L.dit_quant_fp8(a["q8"], a["k8"], a["vt"], a["am"], a["q"], a["k"], a["v"], a["t"], a["h"], a["hd"],
+                               a["cu"], a["ns"], a["mx"], a["vs"], a["dt"], None)
+    assert quant(dt=0) == dit.DIT_E_UNSUPPORTED and "bf16" in _err()
+    assert quant(q8=None) == dit.DIT_E_INVAL
+    assert quant(hd=64) == dit.DIT_E_UNSUPPORTED and "128" in _err()
+    assert quant(vs=vs - 64) == dit.DIT_E_INVAL and "v_stride" in _err()
+    assert quant(vs=vs + 8) == dit.DIT_E_INVAL
+    assert quant(cu=FAKE * 80, ns=2, mx=0) == dit.DIT_E_INVAL and "max_seqlen" in _err()
+    assert quant(q8=q + 64) == dit.DIT_E_INVAL and "overlap" in _err()
+    assert L.dit_attn3d_fp8(None, q8, k8, v8t, am, 64, 2, 128, None, 1, 0, vs, None) == dit.DIT_E_INVAL
+    assert L.dit_attn3d_fp8(q, q8, k8, v8t, am, 64, 2, 64, None, 1, 0, vs, None) == dit.DIT_E_UNSUPPORTED
+    assert L.dit_attn3d_fp8(q8, q8, k8, v8t, am, 64, 2, 128, None, 1, 0, vs, None) == dit.DIT_E_INVAL
+
+
 def test_error_text_is_thread_local_and_cleared_on_new_error():
     L = ensure_built()
     L.rf_euler_step(None, None, None, None, 0, 0, 0, 1, None)
