@@ -28,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 WORKLOAD_KEYS = {"c1": "c1_tiny_f32", "c2": "c2_image_4096_bf16", "c3": "c3_video480p_32760_bf16",
                  "c4": "c4_video720p_27280_bf16", "c5": "c5_varlen_frames_bf16"}
@@ -226,6 +227,42 @@ def main():
                                     for i in range(R)])
     del accs, laccs, obs, lbs
 
+    # 8-bit attention (not part of the bf16 step): E4M3 quantisation of q, k, v (per
+    # head scales, V transposed) and the attention on the codes, same sequences
+    if w.dtype == "bf16" and w.head_dim == 128:
+        vs = dit.dit_fp8_v_stride(w.tokens, w.num_seqs)
+        q8 = torch.empty(q.shape, dtype=torch.uint8, device="cuda")
+        k8 = torch.empty_like(q8)
+        v8t = torch.zeros((w.heads, w.head_dim, vs), dtype=torch.uint8, device="cuda")
+        amax = torch.empty(3, w.heads, dtype=torch.float32, device="cuda")
+        fp8_kw = ({"num_seqs": w.num_seqs, "max_seqlen": w.max_seqlen} if cu is None
+                  else {"cu_seqlens": cu, "max_seqlen": w.max_seqlen})
+
+        def quant():
+            dit.dit_quant_fp8(q8, k8, v8t, amax, q, k, v, **fp8_kw)
+
+        def attn_fp8():
+            dit.dit_attn3d_fp8(o, q8, k8, v8t, amax, **fp8_kw)
+        quant()
+        attn_fp8()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            attn_fp8()
+        e1.record()
+        torch.cuda.synchronize()
+        kern_ms["attn_fp8"] = e0.elapsed_time(e1) / 3
+        # quantisation: reads q, k, v twice (amax, then codes), writes 3 byte-codes
+        quant_bytes = 3 * w.tokens * w.d_model * (2 * esz + 1)
+        R = rotation(quant_bytes)
+        qs_ = [q.clone() for _ in range(R)]
+        q8s = [torch.empty_like(q8) for _ in range(R)]
+
+        def quant_i(i):
+            dit.dit_quant_fp8(q8s[i], k8, v8t, amax, qs_[i], k, v, **fp8_kw)
+        kern_ms["quant_fp8"] = timed_batch([(lambda i=i: quant_i(i)) for i in range(R)])
+        del qs_, q8s, q8, k8, v8t
+
     # flow-matching training side (not part of the sampling step): the straight-path
     # interpolant and the flow-matching loss over the latent
     P_ = synth.LATENT_CHANNELS
@@ -275,12 +312,18 @@ def main():
         "cfm_loss": 3 * tok * P * esz + tok * 4 + w.rows * 4,
         "insert_frames": ins_bytes,
     }
+    if "quant_fp8" in kern_ms:
+        algo_bytes["quant_fp8"] = quant_bytes
     attn_s = kern_ms["attn"] * 1e-3
     achieved = flops / attn_s / 1e12
     traffic = traffic_for(w.name)
     kernels = {"attn": {"us": round(kern_ms["attn"] * 1e3, 2), "tflops": round(achieved, 2)},
                "attn_lse": {"us": round(kern_ms["attn_lse"] * 1e3, 2),
                             "tflops": round(flops / (kern_ms["attn_lse"] * 1e-3) / 1e12, 2)}}
+    if "attn_fp8" in kern_ms:
+        tf8 = flops / (kern_ms["attn_fp8"] * 1e-3) / 1e12
+        kernels["attn_fp8"] = {"us": round(kern_ms["attn_fp8"] * 1e3, 2), "tflops": round(tf8, 2),
+                               "frac_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4)}
     for n, nb in algo_bytes.items():
         gbs = nb / (kern_ms[n] * 1e-3) / 1e9
         kernels[n] = {"us": round(kern_ms[n] * 1e3, 2), "gbs": round(gbs, 1),
