@@ -69,6 +69,13 @@ __device__ __forceinline__ void pin_all_lanes(T& v) {
     asm volatile("" : "+v"(v));
 }
 
+// Thread and block indices straight from the hardware registers. (In kernels
+// this large, the library functions behind threadIdx / blockIdx / gridDim are
+// not inlined: each use became a call, which clobbers registers and costs
+// spills.)
+__device__ __forceinline__ int thread_index() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ unsigned block_index() { return __builtin_amdgcn_workgroup_id_x(); }
+
 // Work item of one block: query tile qt of sequence seq, head head; the
 // sequence's queries start at row s0 (len of them), its keys at row k0 (klen).
 struct BlockWork {
@@ -91,7 +98,7 @@ __device__ __forceinline__ bool decode_block(const int32_t* cu_q, const int32_t*
     int64_t s0, k0;   // first query row / first key row of the sequence
     int len, klen;    // its queries / keys
     if (cu_q == nullptr) {
-        total = (int)gridDim.x;
+        total = nqt * heads * num_seqs;   // the launch's grid
     } else {
         total = 0;
         for (int s = 0; s < num_seqs; ++s) {
@@ -100,7 +107,7 @@ __device__ __forceinline__ bool decode_block(const int32_t* cu_q, const int32_t*
         }
         total *= heads;
     }
-    const int b = (int)blockIdx.x;
+    const int b = (int)block_index();
     if (b >= total) return false;
     {
         const int per = total / 8, rem = total % 8;

@@ -454,7 +454,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     const int q0 = qt * BQ;
     if (q0 >= len) return;
     if (klen == 0) {   // no keys: o = 0, lse = -inf (the empty sum)
-        const int tid = threadIdx.x;
+        const int tid = thread_index();
         for (int i = tid; i < BQ; i += 64 * NW) {
             const int qi = q0 + i;
             if (qi >= len) break;
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     }
 
     Pipe<HD, NW, QB> p;
-    const int tid = threadIdx.x;
+    const int tid = thread_index();
     p.lane = tid & 63;
     p.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     p.g = p.lane >> 5;

@@ -24,8 +24,15 @@
 //   * probabilities are exp2(s - m + 6) with the running max m raised whenever
 //     a tile max exceeds it by more than 2: the largest weight lies in
 //     [2^6, 2^8] (E4M3 holds up to 448), so weights down to 2^-12 of the
-//     largest keep E4M3's full 3-bit precision. The row sum adds the unrounded
-//     probabilities.
+//     largest keep E4M3's full 3-bit precision;
+//   * the exponentials alone take as many cycles per tile as the products (a
+//     quarter-rate instruction per score), so the vector ALU is the bound and
+//     the rest of the softmax is kept off it: the row sums are one more
+//     product per tile, against a constant operand whose row 0 is 1.0 (they
+//     add the same E4M3 probabilities the output product uses); the tile loop
+//     is unrolled over the lcm of the 3-slot rings and the 2 score register
+//     sets, so LDS slot addresses are immediate offsets and no score register
+//     is copied.
 #include <math.h>
 
 #include "dit_attn_common.hpp"
@@ -65,22 +72,36 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f3
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);   // e4m3 x e4m3, scale 1
 }
 
-__device__ __forceinline__ float max16(const f32x16& S) {
-    float mx = __builtin_fmaxf(S[0], __builtin_fmaxf(S[1], S[2]));
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// max of the lane's 32 scores: two interleaved chains of 3-input maxima, 16
+// instructions (left to itself the compiler builds a 25-instruction tree)
+__device__ __forceinline__ float max32(const f32x16 (&S)[2]) {
+    float a = max3(S[0][0], S[0][1], S[0][2]);
+    float b = max3(S[1][0], S[1][1], S[1][2]);
 #pragma unroll
-    for (int r = 3; r < 15; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(S[r], S[r + 1]));
-    return __builtin_fmaxf(mx, S[15]);
+    for (int r = 3; r < 15; r += 2) {
+        a = max3(a, S[0][r], S[0][r + 1]);
+        b = max3(b, S[1][r], S[1][r + 1]);
+    }
+    return max3(a, b, __builtin_fmaxf(S[0][15], S[1][15]));
 }
 
 struct State {
     i32x4 rk, rv;
     int wave, lane, g, len, ntiles;
     uint32_t ldk, koff, voff;
-    uint32_t kaddr[4];   // K operand chunk addresses within a tile: (step i, chunk t) -> 2i + t
-    uint32_t vaddr[2];   // V^T operand chunk addresses within a tile, d block 0
+    uint32_t kaddr[4];   // K operand chunk addresses in ring slot 0: (step i, chunk t) -> 2i + t
+    uint32_t vaddr[2];   // V^T operand chunk addresses in ring slot 0, d block 0
     i32x8 qreg[2];       // Q (B operand of S^T) for head dims 0..63 and 64..127
+    i32x8 ones;          // A operand whose row 0 is E4M3 1.0 at all 64 keys, rows 1..31 zero
     f32x16 O[4];
-    float m_run, l_run, c;
+    f32x16 L;            // row sums: row 0 of L = ones x P (lanes of half 0, register 0)
+    float m_run, c;
 };
 
 // K tile (keys kbase..kbase+63): wave w moves rows 8w..8w+7 (1 KB); lane L
@@ -104,38 +125,56 @@ __device__ __forceinline__ void issue_v(const State& p, char* dst, uint32_t j) {
     dma16(p.rv, lbase, p.voff, 64 * j);
 }
 
-__device__ __forceinline__ void s_tile(const State& p, uint32_t kt, f32x16 (&S)[2]) {
+// The operand addresses are a per-lane part plus a slot offset that is a
+// compile-time constant in the unrolled loop; the offset belongs in the LDS
+// instruction's offset field. A local copy of the per-lane part, redefined by an
+// empty asm (no instruction) in the same block as the reads, keeps the compiler
+// from computing the sums elsewhere (hoisted out of the loop, each in a register
+// of its own, or in a block before the reads where they cannot fold).
+template <int N>
+__device__ __forceinline__ void local_addrs(uint32_t (&a)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(a[i]));
+}
+
+__device__ __forceinline__ void s_tile(State& p, uint32_t slot_off, f32x16 (&S)[2]) {
+    uint32_t (&ka)[4] = p.kaddr;
+    local_addrs(ka);
 #pragma unroll
     for (int r = 0; r < 16; ++r) { S[0][r] = 0.f; S[1][r] = 0.f; }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const uint32_t base = kt + kb * 32 * HD;
-            S[kb] = mfma8(lds_op(base + p.kaddr[2 * i], base + p.kaddr[2 * i + 1]), p.qreg[i], S[kb]);
+            const uint32_t off = slot_off + kb * 32 * HD;
+            S[kb] = mfma8(lds_op(ka[2 * i] + off, ka[2 * i + 1] + off), p.qreg[i], S[kb]);
         }
 }
 
 __device__ __forceinline__ void mask_tile(f32x16 (&S)[2], int g, int kbase, int len) {
+    // keys of the tile that exist; redefined here by an empty asm so that the 32
+    // compares stay in this (once per sequence) branch: the last tile's index is
+    // loop-invariant, and hoisted compares would hold 64 scalar registers per
+    // unrolled step
+    int rem = len - kbase;
+    asm volatile("" : "+s"(rem));
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int k = kbase + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (k >= len) S[0][r] = -INFINITY;
-        if (k + 32 >= len) S[1][r] = -INFINITY;
+        const int k = 8 * (r >> 2) + 4 * g + (r & 3);
+        if (k >= rem) S[0][r] = -INFINITY;
+        if (k + 32 >= rem) S[1][r] = -INFINITY;
     }
 }
 
 // raise the running max (rescaling O and l) when the tile max exceeds it by more
 // than kLazy -- a wave-uniform branch
 __device__ __forceinline__ void max_update(State& p, const f32x16 (&S)[2]) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(__builtin_fmaxf(max16(S[0]), max16(S[1]))),
-                                                    __float_as_uint(__builtin_fmaxf(max16(S[0]), max16(S[1]))),
-                                                    false, false);
-    const float mxs = __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * p.c;
+    const float mxs = pair_max(max32(S)) * p.c;
     if (__builtin_amdgcn_ballot_w64(mxs > p.m_run + kLazy) != 0) {
         const float m_new = __builtin_fmaxf(p.m_run, mxs);
         const float alpha = __builtin_amdgcn_exp2f(p.m_run - m_new);
-        p.l_run *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p.L[r] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -145,8 +184,8 @@ __device__ __forceinline__ void max_update(State& p, const f32x16 (&S)[2]) {
 }
 
 // probabilities of the tile in S as the B operand of O^T += V^T P^T (byte
-// 16b + r of the lane's 32 = score S[b][r]) and their unrounded row sum
-__device__ __forceinline__ i32x8 probs(State& p, const f32x16 (&S)[2]) {
+// 16b + r of the lane's 32 = score S[b][r])
+__device__ __forceinline__ i32x8 probs(const State& p, const f32x16 (&S)[2]) {
     const float off = kPOffset - p.m_run;
     int w[8];
 #pragma unroll
@@ -156,10 +195,11 @@ __device__ __forceinline__ i32x8 probs(State& p, const f32x16 (&S)[2]) {
         for (int e = 0; e < 4; ++e) {
             const int j = 4 * t + e;
             v[e] = __builtin_amdgcn_exp2f(fmaf(S[j >> 4][j & 15], p.c, off));
-            p.l_run += v[e];
         }
-        int d = 0;
-        d = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], d, false);
+        // the first conversion fills bytes 0-1 and keeps bytes 2-3 of its third
+        // operand, which the second one overwrites: any register will do, and
+        // v[0]'s (dead after it) spares a zeroing move
+        int d = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], __float_as_int(v[0]), false);
         d = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], d, true);
         w[t] = d;
     }
@@ -167,17 +207,69 @@ __device__ __forceinline__ i32x8 probs(State& p, const f32x16 (&S)[2]) {
     return r;
 }
 
-__device__ __forceinline__ void pv_tile(State& p, uint32_t vt, const i32x8& P) {
+__device__ __forceinline__ void pv_tile(State& p, uint32_t slot_off, const i32x8& P) {
+    uint32_t (&va)[2] = p.vaddr;
+    local_addrs(va);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-        const uint32_t base = vt + dt * 32 * BK;
-        p.O[dt] = mfma8(lds_op(base + p.vaddr[0], base + p.vaddr[1]), P, p.O[dt]);
+        const uint32_t off = slot_off + dt * 32 * BK;
+        p.O[dt] = mfma8(lds_op(va[0] + off, va[1] + off), P, p.O[dt]);
     }
+    p.L = mfma8(p.ones, P, p.L);
+}
+
+// K and V^T tile rings in LDS (one kernel in this file uses them); addressed
+// directly, so every slot address is a compile-time constant
+__shared__ __attribute__((aligned(1024))) char kring[ST][TILEB];
+__shared__ __attribute__((aligned(1024))) char vring[ST][TILEB];
+
+
+// Step j (j = J mod 6) of the key loop: Sin holds S(j); K(j+1), V(j) are resident
+// in slots (J+1) % 3, J % 3. Issues K(j+3), V(j+2); leaves S(j+1) in Sout.
+template <int J>
+__device__ __forceinline__ void step(State& p, int j, const f32x16 (&Sin)[2], f32x16 (&Sout)[2]) {
+    const int kn = j + 3, vn = j + 2;
+    const bool ik = kn < p.ntiles, iv = vn < p.ntiles;
+    if (ik) issue_k(p, kring[(J + 3) % ST], (uint32_t)kn * BK);
+    if (iv) issue_v(p, vring[(J + 2) % ST], (uint32_t)vn);
+    const i32x8 P = probs(p, Sin);
+    s_tile(p, ((J + 1) % ST) * TILEB, Sout);   // S(j+1): independent of the probabilities above
+    pv_tile(p, (J % ST) * TILEB, P);
+    if (j + 1 == p.ntiles - 1) mask_tile(Sout, p.g, (j + 1) * BK, p.len);
+    max_update(p, Sout);
+    // the next step reads K(j+2), V(j+1), issued one step earlier; this step's
+    // own loads (completing in issue order) may stay in flight
+    if (ik)
+        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if (iv)
+        asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+}
+
+// The same step with run-time slots, S(j) -> S(j+1) in place (the fewer than
+// six steps after the unrolled passes)
+__device__ __forceinline__ void step_rt(State& p, int j, f32x16 (&S)[2]) {
+    const int kn = j + 3, vn = j + 2;
+    const bool ik = kn < p.ntiles, iv = vn < p.ntiles;
+    if (ik) issue_k(p, kring[kn % ST], (uint32_t)kn * BK);
+    if (iv) issue_v(p, vring[vn % ST], (uint32_t)vn);
+    const i32x8 P = probs(p, S);
+    s_tile(p, (uint32_t)((j + 1) % ST) * TILEB, S);
+    pv_tile(p, (uint32_t)(j % ST) * TILEB, P);
+    if (j + 1 == p.ntiles - 1) mask_tile(S, p.g, (j + 1) * BK, p.len);
+    max_update(p, S);
+    if (ik)
+        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if (iv)
+        asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
 }
 
 __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(AttnFp8Args a, int nqt) {
-    __shared__ __attribute__((aligned(1024))) char kbuf[ST][TILEB];
-    __shared__ __attribute__((aligned(1024))) char vbuf[ST][TILEB];
 
     BlockWork bw;
     if (!decode_block(a.cu_seqlens, a.cu_seqlens, a.num_seqs, a.max_seqlen, a.max_seqlen, a.heads, nqt, BQ, bw))
@@ -198,7 +290,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(AttnFp8Args a, int
     }
 
     State p;
-    const int tid = threadIdx.x;
+    const int tid = thread_index();
     p.lane = tid & 63;
     p.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     p.g = p.lane >> 5;
@@ -224,9 +316,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(AttnFp8Args a, int
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-            p.kaddr[2 * i + t] = (uint32_t)(l32 * HD + (((4 * i + 2 * p.g + t) ^ kswz(l32)) * 16));
+            p.kaddr[2 * i + t] = lds_addr(kring[0]) + (uint32_t)(l32 * HD + (((4 * i + 2 * p.g + t) ^ kswz(l32)) * 16));
 #pragma unroll
-    for (int t = 0; t < 2; ++t) p.vaddr[t] = (uint32_t)(l32 * BK + (((2 * p.g + t) ^ vswz(l32)) * 16));
+    for (int t = 0; t < 2; ++t)
+        p.vaddr[t] = lds_addr(vring[0]) + (uint32_t)(l32 * BK + (((2 * p.g + t) ^ vswz(l32)) * 16));
 
     // ---- Q: lane holds query q0 + 32 wave + l32, head dims 64i + 32g .. +31
     const int my_q = q0 + 32 * p.wave + l32;
@@ -244,8 +337,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(AttnFp8Args a, int
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) p.O[dt][r] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p.L[r] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) p.ones[t] = l32 == 0 ? 0x38383838 : 0;   // E4M3 1.0 = 0x38
     p.m_run = -INFINITY;
-    p.l_run = 0.f;
     const float sq = a.amax[head] / kE4M3Max, sk = a.amax[a.heads + head] / kE4M3Max;
     const float sv = a.amax[2 * a.heads + head] / kE4M3Max;
     // log2(e) / sqrt(128); kept >= the smallest normal float so that a head whose q
@@ -255,51 +351,43 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(AttnFp8Args a, int
 
     // ---- prologue: K(0), V(0), K(1) resident; S(0) and its max; then the loads a
     // step -1 would have issued (K(2), V(1))
-    issue_k(p, kbuf[0], 0);
-    issue_v(p, vbuf[0], 0);
-    if (p.ntiles > 1) issue_k(p, kbuf[1], BK);
+    issue_k(p, kring[0], 0);
+    issue_v(p, vring[0], 0);
+    if (p.ntiles > 1) issue_k(p, kring[1], BK);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    f32x16 S[2];
-    s_tile(p, __builtin_amdgcn_readfirstlane(lds_addr(kbuf[0])), S);
-    if (p.ntiles == 1) mask_tile(S, p.g, 0, len);
-    max_update(p, S);
+    f32x16 Sa[2], Sb[2];
+    s_tile(p, 0, Sa);
+    if (p.ntiles == 1) mask_tile(Sa, p.g, 0, len);
+    max_update(p, Sa);
     __syncthreads();   // all reads of K(0) done before its slot is refilled
-    if (p.ntiles > 2) issue_k(p, kbuf[2], 2 * BK);
-    if (p.ntiles > 1) issue_v(p, vbuf[1], 1);
+    if (p.ntiles > 2) issue_k(p, kring[2], 2 * BK);
+    if (p.ntiles > 1) issue_v(p, vring[1], 1);
 
-    // ---- steady state: step j holds S(j); K(j+1), V(j) resident
-    for (int j = 0; j + 1 < p.ntiles; ++j) {
-        const int kn = j + 3, vn = j + 2;
-        const bool ik = kn < p.ntiles, iv = vn < p.ntiles;
-        if (ik) issue_k(p, kbuf[kn % ST], (uint32_t)kn * BK);
-        if (iv) issue_v(p, vbuf[vn % ST], (uint32_t)vn);
-        const uint32_t kt = __builtin_amdgcn_readfirstlane(lds_addr(kbuf[(j + 1) % ST]));
-        const uint32_t vt = __builtin_amdgcn_readfirstlane(lds_addr(vbuf[j % ST]));
-        const i32x8 P = probs(p, S);
-        s_tile(p, kt, S);   // S(j+1): independent of the probabilities above
-        pv_tile(p, vt, P);
-        if (j + 1 == p.ntiles - 1) mask_tile(S, p.g, (j + 1) * BK, len);
-        max_update(p, S);
-        // the next step reads K(j+2), V(j+1), issued one step earlier; this step's
-        // own loads (completing in issue order) may stay in flight
-        if (ik)
-            asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-        else if (iv)
-            asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+    // ---- steady state: passes of six steps (slots and score sets alternate with
+    // compile-time indices, S(j) back in Sa after each pass), then the rest
+    const int steps = p.ntiles - 1;
+    int j = 0;
+    for (; j + 6 <= steps; j += 6) {
+        step<0>(p, j, Sa, Sb);
+        step<1>(p, j + 1, Sb, Sa);
+        step<2>(p, j + 2, Sa, Sb);
+        step<3>(p, j + 3, Sb, Sa);
+        step<4>(p, j + 4, Sa, Sb);
+        step<5>(p, j + 5, Sb, Sa);
     }
+    for (; j < steps; ++j) step_rt(p, j, Sa);
     {
-        const i32x8 P = probs(p, S);
-        pv_tile(p, __builtin_amdgcn_readfirstlane(lds_addr(vbuf[(p.ntiles - 1) % ST])), P);
+        const i32x8 P = probs(p, Sa);
+        pv_tile(p, (uint32_t)((p.ntiles - 1) % ST) * TILEB, P);
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) pin_all_lanes(p.O[dt]);
+    pin_all_lanes(p.L);
 
-    // ---- normalise and store: lane holds query my_q, d = 32dt + 8(r/4) + 4g + r%4
-    const float inv = sv / pair_sum(p.l_run);   // lanes l and l^32 summed disjoint keys
+    // ---- normalise and store: lane holds query my_q, d = 32dt + 8(r/4) + 4g + r%4;
+    // the row sum is row 0 of L (half 0); half 1's register 0 holds row 4 (zero)
+    const float inv = sv / pair_sum(p.L[0]);
     if (my_q < len) {
         uint2* Og = reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(a.o) + base + (int64_t)my_q * a.heads * HD);
 #pragma unroll
