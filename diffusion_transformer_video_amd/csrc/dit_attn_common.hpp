@@ -58,15 +58,27 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(lds_ptr_t)(const_cast<void*>(p));   // LDS byte address
 }
 
-// Materialise v here, with every lane active. A matrix-core product reads its
-// operands only from the active lanes, and the compiler is free to sink the last
-// products of the key loop into the lane-divergent branch of the store that
-// alone consumes them (rows past the sequence end are inactive there), which
-// would silently drop the inactive lanes' rows of V and columns of P. The empty
-// asm consumes and redefines v outside that branch; it emits no instruction.
-template <typename T>
-__device__ __forceinline__ void pin_all_lanes(T& v) {
-    asm volatile("" : "+v"(v));
+// Stores without a lane-divergent branch: a raw buffer store drops every access
+// at or past the resource's record count, so a lane whose row lies past the
+// sequence's end stores to kDropOffset instead of branching around the store. (A
+// divergent branch around the output stores lets the compiler sink the last
+// matrix-core products into it, where a product reads its operands from the
+// active lanes only.)
+constexpr uint32_t kDropOffset = 0xFFFFFFF0u;   // past any record count used with it
+
+__device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, uint2 v, uint32_t off) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 d = {v.x, v.y};
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, float v, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, 0);
+}
+
+// raw buffer resource over `bytes` bytes at p (byte offsets, range-checked)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)bytes, 0x00020000);
 }
 
 // Thread and block indices straight from the hardware registers. (In kernels

@@ -558,33 +558,36 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     for (int j = 0; j + 2 < p.ntiles; ++j) pipe_step<HD, NW, QB, false>(p, j, S, kbuf[0], vbuf[0]);
     if (p.ntiles > 1) pipe_step<HD, NW, QB, true>(p, p.ntiles - 2, S, kbuf[0], vbuf[0]);
     pipe_last<HD, NW, QB>(p, S, lds_addr(vbuf[0]) + ((p.ntiles - 1) % C::ST) * C::TILEB);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) pin_all_lanes(p.O[qb][dt]);
 
     // ---- normalise and store: lane holds query my_q[qb], d = 32dt + 8(r/4) + 4g + r%4;
-    // lanes l and l^32 summed disjoint keys of the same query
+    // lanes l and l^32 summed disjoint keys of the same query.
+    // The sequence's rows of o (and lse) for this head, as range-checked buffers:
+    // rows past its end store to kDropOffset (no lane-divergent branch)
+    const uint32_t ostride = (uint32_t)a.heads * HD * 2;   // bytes per token row of o
+    const __amdgpu_buffer_rsrc_t ro =
+        out_rsrc(reinterpret_cast<__bf16*>(a.o) + (s0 * a.heads + head) * HD, (uint32_t)len * ostride);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l = pair_sum(p.l_run[qb]);
         const float inv = 1.0f / l;
-        if (my_q[qb] < len) {
-            const int64_t row = (s0 + my_q[qb]) * a.heads + head;
-            uint2* Og = reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(a.o) + row * HD);
+        const bool live = my_q[qb] < len;
+        const uint32_t rowoff = (uint32_t)my_q[qb] * ostride;
 #pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) {
+        for (int dt = 0; dt < C::NDT; ++dt) {
 #pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    uint2 wv;
-                    wv.x = pack_bf16x2(p.O[qb][dt][4 * rg + 0] * inv, p.O[qb][dt][4 * rg + 1] * inv);
-                    wv.y = pack_bf16x2(p.O[qb][dt][4 * rg + 2] * inv, p.O[qb][dt][4 * rg + 3] * inv);
-                    Og[(dt * 32 + 8 * rg + 4 * p.g) / 4] = wv;
-                }
+            for (int rg = 0; rg < 4; ++rg) {
+                uint2 wv;
+                wv.x = pack_bf16x2(p.O[qb][dt][4 * rg + 0] * inv, p.O[qb][dt][4 * rg + 1] * inv);
+                wv.y = pack_bf16x2(p.O[qb][dt][4 * rg + 2] * inv, p.O[qb][dt][4 * rg + 3] * inv);
+                bstore8(ro, wv, live ? rowoff + (uint32_t)(dt * 32 + 8 * rg + 4 * p.g) * 2 : kDropOffset);
             }
-            // ln sum_keys exp(s) = ln 2 * (m + log2 l): scores were exponentiated as
-            // exp2(s * log2(e) - m)
-            if (a.lse != nullptr && p.g == 0) a.lse[row] = (p.m_run[qb] + __log2f(l)) * 0.69314718055994531f;
+        }
+        // ln sum_keys exp(s) = ln 2 * (m + log2 l): scores were exponentiated as
+        // exp2(s * log2(e) - m)
+        if (a.lse != nullptr) {
+            const __amdgpu_buffer_rsrc_t rl = out_rsrc(a.lse + s0 * a.heads + head, (uint32_t)len * a.heads * 4);
+            bstore4(rl, (p.m_run[qb] + __log2f(l)) * 0.69314718055994531f,
+                    live && p.g == 0 ? (uint32_t)my_q[qb] * a.heads * 4 : kDropOffset);
         }
     }
 }

@@ -72,23 +72,15 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f3
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);   // e4m3 x e4m3, scale 1
 }
 
-__device__ __forceinline__ float max3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-
-// max of the lane's 32 scores: two interleaved chains of 3-input maxima, 16
-// instructions (left to itself the compiler builds a 25-instruction tree)
+// max of the lane's 32 scores, a left-to-right chain (it compiles to 3-input
+// maxima). No inline asm here: these reads follow the products closely, and the
+// compiler inserts the wait states a vector read of a matrix-core result needs
+// only before instructions it knows.
 __device__ __forceinline__ float max32(const f32x16 (&S)[2]) {
-    float a = max3(S[0][0], S[0][1], S[0][2]);
-    float b = max3(S[1][0], S[1][1], S[1][2]);
+    float a = __builtin_fmaxf(S[0][0], S[1][0]);
 #pragma unroll
-    for (int r = 3; r < 15; r += 2) {
-        a = max3(a, S[0][r], S[0][r + 1]);
-        b = max3(b, S[1][r], S[1][r + 1]);
-    }
-    return max3(a, b, __builtin_fmaxf(S[0][15], S[1][15]));
+    for (int r = 1; r < 16; ++r) a = __builtin_fmaxf(__builtin_fmaxf(a, S[0][r]), S[1][r]);
+    return a;
 }
 
 struct State {
@@ -381,25 +373,24 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(AttnFp8Args a, int
         const i32x8 P = probs(p, Sa);
         pv_tile(p, (uint32_t)((p.ntiles - 1) % ST) * TILEB, P);
     }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) pin_all_lanes(p.O[dt]);
-    pin_all_lanes(p.L);
 
     // ---- normalise and store: lane holds query my_q, d = 32dt + 8(r/4) + 4g + r%4;
     // the row sum is row 0 of L (half 0); half 1's register 0 holds row 4 (zero)
     const float inv = sv / pair_sum(p.L[0]);
-    if (my_q < len) {
-        uint2* Og = reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(a.o) + base + (int64_t)my_q * a.heads * HD);
+    // the sequence's rows of o for this head as a range-checked buffer: rows past
+    // its end store to kDropOffset (no lane-divergent branch)
+    const uint32_t ostride = (uint32_t)a.heads * HD * 2;   // bytes per token row of o
+    const __amdgpu_buffer_rsrc_t ro = out_rsrc(reinterpret_cast<__bf16*>(a.o) + base, (uint32_t)len * ostride);
+    const uint32_t rowoff = (uint32_t)my_q * ostride;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                uint2 wv;
-                wv.x = pack_bf16x2(p.O[dt][4 * rg + 0] * inv, p.O[dt][4 * rg + 1] * inv);
-                wv.y = pack_bf16x2(p.O[dt][4 * rg + 2] * inv, p.O[dt][4 * rg + 3] * inv);
-                Og[(dt * 32 + 8 * rg + 4 * p.g) / 4] = wv;
-            }
-    }
+        for (int rg = 0; rg < 4; ++rg) {
+            uint2 wv;
+            wv.x = pack_bf16x2(p.O[dt][4 * rg + 0] * inv, p.O[dt][4 * rg + 1] * inv);
+            wv.y = pack_bf16x2(p.O[dt][4 * rg + 2] * inv, p.O[dt][4 * rg + 3] * inv);
+            bstore8(ro, wv, my_q < len ? rowoff + (uint32_t)(dt * 32 + 8 * rg + 4 * p.g) * 2 : kDropOffset);
+        }
 }
 
 }  // namespace
