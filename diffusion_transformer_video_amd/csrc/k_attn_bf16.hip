@@ -107,10 +107,9 @@ __device__ __forceinline__ bf16x8 lds_read16(uint32_t a) {
 // tile and block bases ride in the scalar offset. Otherwise rows past the end are
 // clamped to the last row (their scores are masked / probabilities are 0).
 template <int HD, int NW, bool FULL, bool ISV>
-__device__ __forceinline__ void issue(const i32x4& rs, const char* dst, int wave, int lane,
+__device__ __forceinline__ void issue(const i32x4& rs, uint32_t lbase, int wave, int lane,
                                       uint32_t ldb, uint32_t kbase, uint32_t rows_left, uint32_t off) {
     using C = Cfg<HD, NW>;
-    const uint32_t lbase = lds_addr(dst);
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
         const int blk = wave + NW * i;
@@ -129,24 +128,24 @@ __device__ __forceinline__ void issue(const i32x4& rs, const char* dst, int wave
 }
 
 template <int HD, int NW, bool ISV>
-__device__ __forceinline__ void issue_any(const i32x4& rs, const char* dst, int wave, int lane,
+__device__ __forceinline__ void issue_any(const i32x4& rs, uint32_t lbase, int wave, int lane,
                                           uint32_t ldb, uint32_t kbase, uint32_t len, uint32_t off) {
     if (kbase + Cfg<HD, NW>::BK <= len)
-        issue<HD, NW, true, ISV>(rs, dst, wave, lane, ldb, kbase, len - kbase, off);
+        issue<HD, NW, true, ISV>(rs, lbase, wave, lane, ldb, kbase, len - kbase, off);
     else
-        issue<HD, NW, false, ISV>(rs, dst, wave, lane, ldb, kbase, len - kbase, off);
+        issue<HD, NW, false, ISV>(rs, lbase, wave, lane, ldb, kbase, len - kbase, off);
 }
 
 // K operands of one tile: for k-step kk and key block kb, this lane's 16 bytes
 // (row 32kb + l32, logical chunk 2kk + g). All are read up front so their LDS
 // latency hides behind the softmax of the previous tile.
 template <int HD, int NW>
-__device__ __forceinline__ void k_fetch(uint32_t kb, const int (&kaddr)[Cfg<HD, NW>::NKK],
+__device__ __forceinline__ void k_fetch(uint32_t kb, const uint32_t (&kaddr)[Cfg<HD, NW>::NKK],
                                         bf16x8 (&ka)[2 * Cfg<HD, NW>::NKK]) {
     using C = Cfg<HD, NW>;
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) {
-        const uint32_t a = kb + kaddr[kk];
+        const uint32_t a = kaddr[kk] + kb;
         ka[2 * kk] = lds_read16<0>(a);
         ka[2 * kk + 1] = lds_read16<32 * C::ROWB>(a);
     }
@@ -174,7 +173,7 @@ __device__ __forceinline__ void s_mfma(const bf16x8 (&ka)[2 * Cfg<HD, NW>::NKK],
 // S^T as above with the K operands read from LDS just before use (no prefetch
 // registers; with QB = 2 every read already feeds two products).
 template <int HD, int NW, int QB>
-__device__ __forceinline__ void s_tile(uint32_t kb, const int (&kaddr)[Cfg<HD, NW>::NKK],
+__device__ __forceinline__ void s_tile(uint32_t kb, const uint32_t (&kaddr)[Cfg<HD, NW>::NKK],
                                        const bf16x8 (&qreg)[QB][Cfg<HD, NW>::NKK], f32x16 (&S)[QB][2]) {
     using C = Cfg<HD, NW>;
 #pragma unroll
@@ -183,7 +182,7 @@ __device__ __forceinline__ void s_tile(uint32_t kb, const int (&kaddr)[Cfg<HD, N
         for (int r = 0; r < 16; ++r) { S[qb][0][r] = 0.f; S[qb][1][r] = 0.f; }
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) {
-        const uint32_t a = kb + kaddr[kk];
+        const uint32_t a = kaddr[kk] + kb;
         const bf16x8 a0 = lds_read16<0>(a);
         const bf16x8 a1 = lds_read16<32 * C::ROWB>(a);
 #pragma unroll
@@ -208,11 +207,13 @@ __device__ __forceinline__ void mask_tile(f32x16 (&S)[QB][2], int g, int kbase, 
     }
 }
 
-__device__ __forceinline__ float max16(const f32x16& S) {
-    float mx = __builtin_fmaxf(S[0], __builtin_fmaxf(S[1], S[2]));
+// a left-to-right chain: it compiles to 3-input maxima (a balanced tree of
+// pairs does not)
+__device__ __forceinline__ float max32(const f32x16& S0, const f32x16& S1) {
+    float mx = __builtin_fmaxf(S0[0], S1[0]);
 #pragma unroll
-    for (int r = 3; r < 15; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(S[r], S[r + 1]));
-    return __builtin_fmaxf(mx, S[15]);
+    for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(__builtin_fmaxf(mx, S0[r]), S1[r]);
+    return mx;
 }
 
 // Online-softmax bookkeeping of one tile for one query block: the scaled tile
@@ -220,7 +221,7 @@ __device__ __forceinline__ float max16(const f32x16& S) {
 // tile max exceeds it by more than 2^kLazyRescale (raise_max; wave-uniform
 // branch).
 __device__ __forceinline__ float tile_max(const f32x16& S0, const f32x16& S1, float c) {
-    return pair_max(__builtin_fmaxf(max16(S0), max16(S1))) * c;
+    return pair_max(max32(S0, S1)) * c;
 }
 
 template <int NDT>
@@ -307,12 +308,12 @@ __device__ __forceinline__ void pv_mfma(const bf16x8 (&v)[Cfg<HD, NW>::NDT], con
 }
 
 template <int HD, int NW, int QB>
-__device__ __forceinline__ void pv_tile(uint32_t vread, const int (&vaddr)[Cfg<HD, NW>::NDT],
+__device__ __forceinline__ void pv_tile(uint32_t vread, const uint32_t (&vaddr)[Cfg<HD, NW>::NDT],
                                         const bf16x8 (&P)[QB][4], f32x16 (&O)[QB][Cfg<HD, NW>::NDT]) {
     using C = Cfg<HD, NW>;
     uint32_t vb[C::NDT];
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) vb[dt] = vread + vaddr[dt];
+    for (int dt = 0; dt < C::NDT; ++dt) vb[dt] = vaddr[dt] + vread;
     pv_step<HD, NW, QB, 0, 0>(vb, P, O);
     pv_step<HD, NW, QB, 0, 1>(vb, P, O);
     pv_step<HD, NW, QB, 1, 0>(vb, P, O);
@@ -326,8 +327,9 @@ struct Pipe {
     i32x4 rk, rv;
     int wave, lane, g, len, qlen, ntiles;   // len: keys of the sequence; qlen: its queries
     uint32_t ldb, koff, voff;
-    int kaddr[C::NKK];
-    int vaddr[C::NDT];
+    uint32_t kring, vring;      // LDS addresses of the K and V tile rings
+    uint32_t kaddr[C::NKK];     // K operand addresses in ring slot 0 (ring base included)
+    uint32_t vaddr[C::NDT];     // V^T operand addresses in ring slot 0
     bf16x8 qreg[QB][C::NKK];
     f32x16 O[QB][C::NDT];
     float m_run[QB], l_run[QB];
@@ -364,47 +366,54 @@ __device__ __forceinline__ void rowsum_tile(Pipe<HD, NW, QB>& p, const bf16x8 (&
         for (int i = 0; i < 4; ++i) rowsum8(P[qb][i], p.l_run[qb]);
 }
 
-// One pipeline step for tile j (S = S(j) in registers with the running max
+// One pipeline step for tile j (Sin = S(j) in registers with the running max
 // already raised for it; K(j+1) and V(j) resident): stream K(j+ST) and V(j+ST-1)
 // into their ring slots; P(j) on the vector ALU while the matrix cores compute
-// S(j+1) = K(j+1) Q^T; O += V(j) P(j) while the vector ALU forms the row sums of
-// P(j) and the max of S(j+1) (masked first when it is the last tile, LAST) -- so
-// the rarely taken rescale branch comes after all of the step's products are
-// issued and never splits them from the softmax work; finally wait for the
-// tiles the next step needs and publish them with a barrier. Requires
-// j+1 < ntiles.
+// S(j+1) = K(j+1) Q^T into Sout; O += V(j) P(j) while the vector ALU forms the
+// row sums of P(j) and the max of S(j+1) (masked first when it is the last
+// tile, LAST) -- so the rarely taken rescale branch comes after all of the
+// step's products are issued and never splits them from the softmax work;
+// finally wait for the tiles the next step needs and publish them with a
+// barrier. Requires j+1 < ntiles. kslot / vslot: byte offsets of ring slots
+// (j+1) % ST and j % ST; compile-time constants in the unrolled loop, where they
+// fold into the LDS instructions' offset fields.
 template <int HD, int NW, int QB, bool LAST>
-__device__ __forceinline__ void pipe_step(Pipe<HD, NW, QB>& p, int j, f32x16 (&S)[QB][2], char* kring,
-                                          char* vring) {
+__device__ __forceinline__ void pipe_step(Pipe<HD, NW, QB>& p, int j, const f32x16 (&Sin)[QB][2],
+                                          f32x16 (&Sout)[QB][2], uint32_t kslot, uint32_t vslot,
+                                          uint32_t kslot_next, uint32_t vslot_next) {
     using C = Cfg<HD, NW>;
     const int kn = j + C::ST, vn = j + C::ST - 1;   // tiles streamed in this step
     const bool issue_k = kn < p.ntiles, issue_v = vn < p.ntiles;
     if (issue_k)
-        issue_any<HD, NW, false>(p.rk, kring + (kn % C::ST) * C::TILEB, p.wave, p.lane, p.ldb,
-                                 (uint32_t)kn * C::BK, (uint32_t)p.len, p.koff);
+        issue_any<HD, NW, false>(p.rk, p.kring + kslot_next, p.wave, p.lane, p.ldb, (uint32_t)kn * C::BK,
+                                 (uint32_t)p.len, p.koff);
     if (issue_v)
-        issue_any<HD, NW, true>(p.rv, vring + (vn % C::ST) * C::TILEB, p.wave, p.lane, p.ldb,
-                                (uint32_t)vn * C::BK, (uint32_t)p.len, p.voff);
-    // ring slot bases as opaque scalars: otherwise loop strength reduction turns
-    // every lane address into its own induction variable with a wrap correction
-    const uint32_t kread = __builtin_amdgcn_readfirstlane(lds_addr(kring) + ((j + 1) % C::ST) * C::TILEB);
-    const uint32_t vread = __builtin_amdgcn_readfirstlane(lds_addr(vring) + (j % C::ST) * C::TILEB);
+        issue_any<HD, NW, true>(p.rv, p.vring + vslot_next, p.wave, p.lane, p.ldb, (uint32_t)vn * C::BK,
+                                (uint32_t)p.len, p.voff);
+    // the per-lane operand addresses, redefined here by an empty asm (no
+    // instruction) at the head of the block that reads them: the slot offsets then
+    // fold into the reads instead of every (address + offset) sum being hoisted out
+    // of the loop into a register of its own
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) asm volatile("" : "+v"(p.kaddr[kk]));
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+v"(p.vaddr[dt]));
     bf16x8 P[QB][4];
     if constexpr (QB == 1 && NW == 4) {   // registers to spare: read all K operands first
         bf16x8 ka[2 * C::NKK];
-        k_fetch<HD, NW>(kread, p.kaddr, ka);
-        probs_tile<HD, NW, QB>(p, S, P);
-        s_mfma<HD, NW, QB>(ka, p.qreg, S);   // S(j+1): independent of the exps above
+        k_fetch<HD, NW>(kslot, p.kaddr, ka);
+        probs_tile<HD, NW, QB>(p, Sin, P);
+        s_mfma<HD, NW, QB>(ka, p.qreg, Sout);   // S(j+1): independent of the exps above
     } else {
-        probs_tile<HD, NW, QB>(p, S, P);
-        s_tile<HD, NW, QB>(kread, p.kaddr, p.qreg, S);   // S(j+1): independent of the exps above
+        probs_tile<HD, NW, QB>(p, Sin, P);
+        s_tile<HD, NW, QB>(kslot, p.kaddr, p.qreg, Sout);   // S(j+1): independent of the exps above
     }
-    pv_tile<HD, NW, QB>(vread, p.vaddr, P, p.O);
+    pv_tile<HD, NW, QB>(vslot, p.vaddr, P, p.O);
     rowsum_tile<HD, NW, QB>(p, P);
-    if constexpr (LAST) mask_tile<QB>(S, p.g, (j + 1) * C::BK, p.len);
+    if constexpr (LAST) mask_tile<QB>(Sout, p.g, (j + 1) * C::BK, p.len);
     float mxs[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mxs[qb] = tile_max(S[qb][0], S[qb][1], p.c);
+    for (int qb = 0; qb < QB; ++qb) mxs[qb] = tile_max(Sout[qb][0], Sout[qb][1], p.c);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) raise_max<C::NDT>(mxs[qb], p.O[qb], p.m_run[qb], p.l_run[qb]);
     // the next step reads K(j+2) and V(j+1): with a 2-deep ring they were issued in
@@ -422,6 +431,31 @@ __device__ __forceinline__ void pipe_step(Pipe<HD, NW, QB>& p, int j, f32x16 (&S
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();   // everyone's loads have landed; all reads of tile j are done
+}
+
+// Step j of the unrolled loop: J = j mod 6 (a multiple of the ring depth and of
+// the two score register sets) fixes the ring slots at compile time.
+template <int HD, int NW, int QB, int J>
+__device__ __forceinline__ void pipe_step_u(Pipe<HD, NW, QB>& p, int j, const f32x16 (&Sin)[QB][2],
+                                            f32x16 (&Sout)[QB][2]) {
+    using C = Cfg<HD, NW>;
+    pipe_step<HD, NW, QB, false>(p, j, Sin, Sout, ((J + 1) % C::ST) * C::TILEB, (J % C::ST) * C::TILEB,
+                                 ((J + C::ST) % C::ST) * C::TILEB, ((J + C::ST - 1) % C::ST) * C::TILEB);
+}
+
+// Step j with run-time ring slots, S(j) -> S(j+1) in place (the steps after the
+// unrolled passes, and the last one, which masks).
+template <int HD, int NW, int QB, bool LAST>
+__device__ __forceinline__ void pipe_step_rt(Pipe<HD, NW, QB>& p, int j, f32x16 (&S)[QB][2]) {
+    using C = Cfg<HD, NW>;
+    const uint32_t ks = __builtin_amdgcn_readfirstlane(((j + 1) % C::ST) * C::TILEB);
+    const uint32_t vs = __builtin_amdgcn_readfirstlane((j % C::ST) * C::TILEB);
+    const uint32_t kn = __builtin_amdgcn_readfirstlane(((j + C::ST) % C::ST) * C::TILEB);
+    const uint32_t vn = __builtin_amdgcn_readfirstlane(((j + C::ST - 1) % C::ST) * C::TILEB);
+    f32x16 Sn[QB][2];
+    pipe_step<HD, NW, QB, LAST>(p, j, S, Sn, ks, vs, kn, vn);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) { S[qb][0] = Sn[qb][0]; S[qb][1] = Sn[qb][1]; }
 }
 
 // Final tile (S = S(j) in registers, running max raised for it; V(j) at LDS
@@ -494,9 +528,11 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
         p.koff = (uint32_t)lrow * p.ldb + (uint32_t)((pc ^ kswz<C::CPR>(lrow)) * 16);
         p.voff = (uint32_t)lrow * p.ldb + (uint32_t)((pc ^ vswz<C::CPR>(lrow)) * 16);
     }
+    p.kring = lds_addr(kbuf[0]);
+    p.vring = lds_addr(vbuf[0]);
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk)
-        p.kaddr[kk] = l32 * C::ROWB + (((2 * kk + p.g) ^ kswz<C::CPR>(l32)) * 16);
+        p.kaddr[kk] = p.kring + (uint32_t)(l32 * C::ROWB + (((2 * kk + p.g) ^ kswz<C::CPR>(l32)) * 16));
     {
         // V^T operand (A of O^T): 16-lane group hg = lane/16 covers d = 32dt + 16(hg%2) + i
         // (i = lane%16); its source lanes point at key row 4g + i/4 (+ step offsets),
@@ -506,7 +542,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) {
             const int d0 = 32 * dt + 16 * (hg & 1) + 4 * (i16 & 3);
-            p.vaddr[dt] = vrow * C::ROWB + ((d0 / 8) ^ vswz<C::CPR>(vrow)) * 16 + (d0 % 8) * 2;
+            p.vaddr[dt] = p.vring + (uint32_t)(vrow * C::ROWB + ((d0 / 8) ^ vswz<C::CPR>(vrow)) * 16 + (d0 % 8) * 2);
         }
     }
 
@@ -531,16 +567,16 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
 
     // ---- prologue: K(0), V(0), K(1) resident; S(0); then the loads a step -1
     // would have issued (K(ST-1), V(ST-2)) for a 3-deep ring
-    issue_any<HD, NW, false>(p.rk, kbuf[0], p.wave, p.lane, p.ldb, 0, (uint32_t)klen, p.koff);
-    issue_any<HD, NW, true>(p.rv, vbuf[0], p.wave, p.lane, p.ldb, 0, (uint32_t)klen, p.voff);
+    issue_any<HD, NW, false>(p.rk, p.kring, p.wave, p.lane, p.ldb, 0, (uint32_t)klen, p.koff);
+    issue_any<HD, NW, true>(p.rv, p.vring, p.wave, p.lane, p.ldb, 0, (uint32_t)klen, p.voff);
     if (p.ntiles > 1)
-        issue_any<HD, NW, false>(p.rk, kbuf[1], p.wave, p.lane, p.ldb, C::BK, (uint32_t)klen, p.koff);
+        issue_any<HD, NW, false>(p.rk, p.kring + C::TILEB, p.wave, p.lane, p.ldb, C::BK, (uint32_t)klen, p.koff);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    f32x16 S[QB][2];
+    f32x16 S[QB][2], Sb[QB][2];
     {
         bf16x8 ka[2 * C::NKK];
-        k_fetch<HD, NW>(lds_addr(kbuf[0]), p.kaddr, ka);
+        k_fetch<HD, NW>(0, p.kaddr, ka);
         s_mfma<HD, NW, QB>(ka, p.qreg, S);
     }
     if (p.ntiles == 1) mask_tile<QB>(S, p.g, 0, klen);
@@ -549,15 +585,28 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     __syncthreads();
     if constexpr (C::ST == 3) {
         if (p.ntiles > 2)
-            issue_any<HD, NW, false>(p.rk, kbuf[2], p.wave, p.lane, p.ldb, 2 * C::BK, (uint32_t)klen, p.koff);
+            issue_any<HD, NW, false>(p.rk, p.kring + 2 * C::TILEB, p.wave, p.lane, p.ldb, 2 * C::BK,
+                                     (uint32_t)klen, p.koff);
         if (p.ntiles > 1)
-            issue_any<HD, NW, true>(p.rv, vbuf[1], p.wave, p.lane, p.ldb, C::BK, (uint32_t)klen, p.voff);
+            issue_any<HD, NW, true>(p.rv, p.vring + C::TILEB, p.wave, p.lane, p.ldb, C::BK, (uint32_t)klen,
+                                    p.voff);
     }
 
-    // ---- steady state: step j reads K(j+1), V(j) from ring slots (j+1) % ST, j % ST
-    for (int j = 0; j + 2 < p.ntiles; ++j) pipe_step<HD, NW, QB, false>(p, j, S, kbuf[0], vbuf[0]);
-    if (p.ntiles > 1) pipe_step<HD, NW, QB, true>(p, p.ntiles - 2, S, kbuf[0], vbuf[0]);
-    pipe_last<HD, NW, QB>(p, S, lds_addr(vbuf[0]) + ((p.ntiles - 1) % C::ST) * C::TILEB);
+    // ---- steady state: step j reads K(j+1), V(j) from ring slots (j+1) % ST, j % ST;
+    // passes of six steps with compile-time slots (S(j) back in S after each
+    // pass), the remaining steps with run-time slots, the masked last step
+    int j = 0;
+    for (; j + 6 <= p.ntiles - 2; j += 6) {
+        pipe_step_u<HD, NW, QB, 0>(p, j, S, Sb);
+        pipe_step_u<HD, NW, QB, 1>(p, j + 1, Sb, S);
+        pipe_step_u<HD, NW, QB, 2>(p, j + 2, S, Sb);
+        pipe_step_u<HD, NW, QB, 3>(p, j + 3, Sb, S);
+        pipe_step_u<HD, NW, QB, 4>(p, j + 4, S, Sb);
+        pipe_step_u<HD, NW, QB, 5>(p, j + 5, Sb, S);
+    }
+    for (; j < p.ntiles - 2; ++j) pipe_step_rt<HD, NW, QB, false>(p, j, S);
+    if (p.ntiles > 1) pipe_step_rt<HD, NW, QB, true>(p, p.ntiles - 2, S);
+    pipe_last<HD, NW, QB>(p, S, (uint32_t)((p.ntiles - 1) % C::ST) * C::TILEB);
 
     // ---- normalise and store: lane holds query my_q[qb], d = 32dt + 8(r/4) + 4g + r%4;
     // lanes l and l^32 summed disjoint keys of the same query.
