@@ -152,7 +152,8 @@ def main():
     t1.record()
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
-    kern_ms = {"attn": float(np.mean([a.elapsed_time(bb) for a, bb in attn_ev]))}
+    attn_each = [a.elapsed_time(bb) for a, bb in attn_ev]
+    kern_ms = {"attn": float(np.mean(attn_each))}
 
     # the short bandwidth-bound kernels: batches of back-to-back launches between two
     # events (a single launch is too short for an event pair to time it faithfully),
@@ -272,6 +273,32 @@ def main():
         kern_ms["quant_fp8"] = timed_batch([(lambda i=i: quant_i(i)) for i in range(R)])
         del qs_, q8s, q8, k8, v8t
 
+    # one GPU's share of Ulysses context parallelism at the 480P video workload on 8
+    # GPUs (all 32,760 tokens, 40 / 8 = 5 heads): the attention each GPU runs
+    # between the two all-to-alls (the collectives themselves are not part of
+    # this single-GPU build)
+    if w.dtype == "bf16" and w.head_dim == 128:
+        ush = (32760, 5, 128)
+        gen = torch.Generator(device="cuda").manual_seed(1003)
+        uq, uk, uv = (torch.randn(ush, device="cuda", generator=gen).to(torch.bfloat16) for _ in range(3))
+        uo = torch.empty_like(uq)
+
+        def attn_share():
+            dit.dit_attn3d(uo, uq, uk, uv, num_seqs=1)
+        attn_share()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            attn_share()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            attn_share()
+        e1.record()
+        torch.cuda.synchronize()
+        kern_ms["attn_ulysses_share"] = e0.elapsed_time(e1) / 5
+        ulysses_flops = 4 * 32760 ** 2 * 5 * 128
+        del uq, uk, uv, uo
+
     # flow-matching training side (not part of the sampling step): the straight-path
     # interpolant and the flow-matching loss over the latent
     P_ = synth.LATENT_CHANNELS
@@ -326,9 +353,16 @@ def main():
     attn_s = kern_ms["attn"] * 1e-3
     achieved = flops / attn_s / 1e12
     traffic = traffic_for(w.name)
-    kernels = {"attn": {"us": round(kern_ms["attn"] * 1e3, 2), "tflops": round(achieved, 2)},
+    kernels = {"attn": {"us": round(kern_ms["attn"] * 1e3, 2), "tflops": round(achieved, 2),
+                        "us_median": round(float(np.median(attn_each)) * 1e3, 2),
+                        "us_min": round(float(np.min(attn_each)) * 1e3, 2),
+                        "us_max": round(float(np.max(attn_each)) * 1e3, 2), "launches": len(attn_each)},
                "attn_lse": {"us": round(kern_ms["attn_lse"] * 1e3, 2),
                             "tflops": round(flops / (kern_ms["attn_lse"] * 1e-3) / 1e12, 2)}}
+    if "attn_ulysses_share" in kern_ms:
+        tu = ulysses_flops / (kern_ms["attn_ulysses_share"] * 1e-3) / 1e12
+        kernels["attn_ulysses_share"] = {"us": round(kern_ms["attn_ulysses_share"] * 1e3, 2), "tflops": round(tu, 2),
+                                         "shape": "32760 tokens x 5 heads x 128 (480P video, 8-way Ulysses share)"}
     if "attn_fp8" in kern_ms:
         tf8 = flops / (kern_ms["attn_fp8"] * 1e-3) / 1e12
         kernels["attn_fp8"] = {"us": round(kern_ms["attn_fp8"] * 1e3, 2), "tflops": round(tf8, 2),
