@@ -6,19 +6,23 @@
 // and the same rotation R_3D(t', h', w') is applied to q and k of every head.
 //
 // HBM-bound: q and k are each read and written once (8 bytes per bf16 element
-// of q when both are rotated). One wave owns one token: the integer
-// token -> (sequence, t', h', w') map is computed once per wave; each lane owns
-// one 8-value chunk of the head vector (4 pairs) and evaluates the 4 pair angles
-// once, then rotates that chunk in every head of q and k (64 / (head_dim/8)
-// heads per pass, so a pass is one contiguous, coalesced span of the token row).
+// of q when both are rotated). One wave owns up to kHeadsPerWave heads of one
+// token (a token's heads are split evenly over ceil(heads / kHeadsPerWave)
+// waves: a wave streaming a whole 24- or 40-head token row reached only 59-64%
+// of HBM bandwidth, 8-head shares 63-70%). The integer token -> (sequence, t',
+// h', w') map is computed once per wave; each lane owns one 8-value chunk of
+// the head vector (4 pairs) and evaluates the 4 pair angles once, then rotates
+// that chunk in each of the wave's heads of q and k (64 / (head_dim/8) heads
+// per pass, so a pass is one contiguous, coalesced span of the token row).
 #include "dit_device.hpp"
 #include "dit_internal.h"
 
 namespace dit {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kUnroll = 4;
+constexpr int kWaves = 8;
+constexpr int kUnroll = 2;
+constexpr int kHeadsPerWave = 8;
 
 __device__ __forceinline__ void rotate8(float (&f)[8], const float (&cs)[4], const float (&sn)[4]) {
 #pragma unroll
@@ -32,7 +36,10 @@ __device__ __forceinline__ void rotate8(float (&f)[8], const float (&cs)[4], con
 template <bool BF16>
 __global__ __launch_bounds__(64 * kWaves) void rope3d_kernel(RopeArgs a) {
     const int lane = threadIdx.x & 63;
-    const int64_t tok = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int split = (a.heads + kHeadsPerWave - 1) / kHeadsPerWave;   // waves per token
+    const int64_t wv = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t tok = wv / split;
+    const int part = (int)(wv - tok * split);
     if (tok >= a.tokens) return;
 
     // token -> position within its sequence
@@ -52,7 +59,7 @@ __global__ __launch_bounds__(64 * kWaves) void rope3d_kernel(RopeArgs a) {
     const int pt = (int)(n / hw);
     const int ph = (int)((n / a.grid_w) % a.grid_h);
     const int pw = (int)(n % a.grid_w);
-    if (a.pos_out != nullptr && lane == 0) {
+    if (a.pos_out != nullptr && lane == 0 && part == 0) {
         a.pos_out[3 * tok + 0] = pt;
         a.pos_out[3 * tok + 1] = ph;
         a.pos_out[3 * tok + 2] = pw;
@@ -80,14 +87,16 @@ __global__ __launch_bounds__(64 * kWaves) void rope3d_kernel(RopeArgs a) {
     }
 
     const int64_t tok_chunk = tok * (int64_t)a.heads * cph;
-    // kUnroll passes of the heads at a time: all their loads are issued before the
-    // first rotation, so each lane keeps 2 * kUnroll 16-byte loads in flight
-    for (int h0 = hsub; h0 < a.heads; h0 += kUnroll * hpp) {
+    // this wave's heads [hb, he); kUnroll passes at a time: all their loads are
+    // issued before the first rotation, so each lane keeps 2 * kUnroll 16-byte
+    // loads in flight
+    const int hb = (a.heads * part) / split, he = (a.heads * (part + 1)) / split;
+    for (int h0 = hb + hsub; h0 < he; h0 += kUnroll * hpp) {
         Packed8<BF16> qv[kUnroll], kv[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int h = h0 + u * hpp;
-            if (h < a.heads) {
+            if (h < he) {
                 const int64_t idx = tok_chunk + (int64_t)h * cph + c;
                 qv[u].load(a.q, idx);
                 if (a.k != nullptr) kv[u].load(a.k, idx);
@@ -96,7 +105,7 @@ __global__ __launch_bounds__(64 * kWaves) void rope3d_kernel(RopeArgs a) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int h = h0 + u * hpp;
-            if (h < a.heads) {
+            if (h < he) {
                 const int64_t idx = tok_chunk + (int64_t)h * cph + c;
                 float f[8];
                 qv[u].unpack(f);
@@ -115,7 +124,9 @@ __global__ __launch_bounds__(64 * kWaves) void rope3d_kernel(RopeArgs a) {
 }  // namespace
 
 hipError_t launch_rope3d(const RopeArgs& a, bool bf16, hipStream_t s) {
-    const dim3 grid((unsigned)((a.tokens + kWaves - 1) / kWaves));
+    const int64_t waves = a.tokens * ((a.heads + kHeadsPerWave - 1) / kHeadsPerWave);
+    if (waves > (int64_t)0x7fffffff * kWaves) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
     const dim3 block(64 * kWaves);
     if (bf16)
         hipLaunchKernelGGL(rope3d_kernel<true>, grid, block, 0, s, a);
