@@ -9,10 +9,11 @@
 // section names beside Euler.
 //
 // Both are HBM-bound streams (6 bytes per bf16 element). The residual runs as
-// column strips: a thread owns one 8-column chunk and walks kTokPerThread
-// consecutive tokens (all loads issued up front, kept in storage format), so the
-// alpha chunk (a per-sample / per-frame row) is read once per strip instead of
-// once per element; threads are numbered chunk-fastest over (strip, chunk). The Euler part is a flat stream
+// short column strips: a thread owns one 8-column chunk of kTokPerThread
+// consecutive tokens (loads issued up front, kept in storage format) and reads
+// the alpha chunk (a per-sample / per-frame row) once per strip; threads are
+// numbered chunk-fastest over (strip, chunk). More threads with fewer loads each
+// stream faster than long strips. The Euler part is a flat stream
 // of 8-value chunks. In the fused launch the first blocks run the residual and
 // the remaining blocks the Euler update: two disjoint passes, one launch.
 #include "dit_device.hpp"
@@ -22,7 +23,7 @@ namespace dit {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokPerThread = 8;
+constexpr int kTokPerThread = 2;   // 8 per thread ran at 62-70% of HBM, 1-2 at 70-77%
 constexpr int kEulerChunksPerThread = 2;
 
 template <bool BF16>
