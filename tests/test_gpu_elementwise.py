@@ -64,6 +64,20 @@ def test_modulate_wide(w):
     _modulate_case(w)
 
 
+# 16K+ wide bf16 rows: each row split over two waves, 8 rows per block; a ragged
+# last block (16,389 rows), a width whose halves differ (257 chunks: 129 + 128),
+# blocks straddling parameter rows (9 and 20 tokens per row), the widest row
+WIDE_MANY = [
+    synth.custom("pairs2056_ragged", "bf16", (27, 607), (1,), 257, 8, (4, 2, 2), tokens_per_row=9),
+    synth.custom("pairs8192_rows20", "bf16", (41, 400), (1,), 64, 128, (44, 42, 42), tokens_per_row=20),
+]
+
+
+@pytest.mark.parametrize("w", WIDE_MANY, ids=lambda w: w.name)
+def test_modulate_wide_many_rows(w):
+    _modulate_case(w, sample_rows(w, per_seq=2048, edge=64))
+
+
 @pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
 def test_modulate_full(w):
     _modulate_case(w, sample_rows(w, per_seq=512) if w.tokens > 20000 else None)
