@@ -64,15 +64,34 @@ __global__ __launch_bounds__(kThreads) void cfm_token_kernel(CfmArgs a) {
     if (tok < a.tokens && sub == 0) a.loss_tok[tok] = acc;
 }
 
-__global__ __launch_bounds__(kThreads) void cfm_row_kernel(CfmArgs a) {
-    __shared__ float red[kThreads];
+// Per-row sums of the token losses: one block of kRowThreads per row; each thread
+// keeps kRowAcc independent partial sums (kRowAcc loads in flight), added in a
+// fixed order, then a fixed LDS tree -- deterministic. (A single long row, as at
+// the 480P workload, is the latency-bound case: one serial load chain per
+// thread took 36 us for 32,760 values.)
+constexpr int kRowThreads = 1024;
+constexpr int kRowAcc = 8;
+
+__global__ __launch_bounds__(kRowThreads) void cfm_row_kernel(CfmArgs a) {
+    __shared__ float red[kRowThreads];
     const int64_t row = blockIdx.x;
-    const int64_t t0 = row * a.tokens_per_row;
-    float acc = 0.f;
-    for (int64_t i = threadIdx.x; i < a.tokens_per_row; i += kThreads) acc += a.loss_tok[t0 + i];
-    red[threadIdx.x] = acc;
+    const int64_t t0 = row * a.tokens_per_row, n = a.tokens_per_row;
+    float acc[kRowAcc];
+#pragma unroll
+    for (int j = 0; j < kRowAcc; ++j) acc[j] = 0.f;
+    for (int64_t base = 0; base < n; base += (int64_t)kRowThreads * kRowAcc) {
+#pragma unroll
+        for (int j = 0; j < kRowAcc; ++j) {
+            const int64_t i = base + (int64_t)j * kRowThreads + threadIdx.x;
+            if (i < n) acc[j] += a.loss_tok[t0 + i];
+        }
+    }
+    float sum = acc[0];
+#pragma unroll
+    for (int j = 1; j < kRowAcc; ++j) sum += acc[j];
+    red[threadIdx.x] = sum;
     __syncthreads();
-    for (int w = kThreads / 2; w > 0; w >>= 1) {
+    for (int w = kRowThreads / 2; w > 0; w >>= 1) {
         if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
@@ -101,7 +120,7 @@ hipError_t launch_cfm_loss(const CfmArgs& a, bool bf16, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.loss_rows == nullptr) return e;
     const int64_t rows = a.tokens / a.tokens_per_row;
-    hipLaunchKernelGGL(cfm_row_kernel, dim3((unsigned)rows), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(cfm_row_kernel, dim3((unsigned)rows), dim3(kRowThreads), 0, s, a);
     return hipGetLastError();
 }
 
