@@ -28,8 +28,14 @@ HIP_FLAGS = [
 
 # Per-file extra flags. Attention never sees NaN inputs (finite scores, -inf only
 # for masked keys), so IEEE-mode NaN quieting before every max is dropped there.
+# The bf16 key loop is also scheduled with the memory-clause strategy and without
+# the post-register-allocation reordering: same instructions, same results, and
+# 2-3% faster (the exponentials spread evenly between the score products, K
+# operand reads issued in pairs).
 FILE_FLAGS = {
-    "k_attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "k_attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
+                        "-mllvm", "-amdgpu-sched-strategy=max-memory-clause",
+                        "-mllvm", "-enable-post-misched=false"],
     "k_attn_fp8.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
 }
 
