@@ -32,7 +32,10 @@ PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 WORKLOAD_KEYS = {"c1": "c1_tiny_f32", "c2": "c2_image_4096_bf16", "c3": "c3_video480p_32760_bf16",
                  "c4": "c4_video720p_27280_bf16", "c5": "c5_varlen_frames_bf16"}
-ATTN_SRC = os.path.join(ROOT, "diffusion_transformer_video_amd", "csrc", "k_attn_bf16.hip")
+CSRC = os.path.join(ROOT, "diffusion_transformer_video_amd", "csrc")
+# what the bf16 attention kernel's machine code is built from
+ATTN_SRCS = [os.path.join(CSRC, f) for f in ("k_attn_bf16.hip", "dit_attn_common.hpp", "dit_device.hpp",
+                                            "dit_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -55,8 +58,15 @@ def parse():
     return p.parse_args()
 
 
-def source_sha(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def kernel_sha():
+    """Hash of the bf16 attention kernel's sources and its per-file compile flags:
+    hardware-counter figures belong to one build of the kernel."""
+    from diffusion_transformer_video_amd import build as _build
+    h = hashlib.sha256()
+    for p in ATTN_SRCS:
+        h.update(open(p, "rb").read())
+    h.update(repr(_build.FILE_FLAGS.get("k_attn_bf16.hip", [])).encode())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(workload):
@@ -67,7 +77,7 @@ def traffic_for(workload):
     except (OSError, ValueError):
         return None
     e = t.get(workload)
-    if not e or e.get("source_sha") != source_sha(ATTN_SRC):
+    if not e or e.get("source_sha") != kernel_sha():
         return None
     return e.get("traffic_bytes_per_launch")
 
