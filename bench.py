@@ -11,8 +11,7 @@ HBM before timing starts.
 Prints ONE JSON line. value = attention FLOPs per step / wall time per step
 (whole path), in TFLOP/s. roofline = the attention kernel's own rate, timed with
 HIP events (without the system-scope fence) around each of its launches on the
-stream it runs on, against the
-2.5 PFLOP/s dense bf16 MFMA peak. cpu_baseline = the float64 numpy oracle on a
+stream it runs on, against the 2.5 PFLOP/s dense bf16 MFMA peak. cpu_baseline = the float64 numpy oracle on a
 bounded sample of the same workload, scaled to the whole step.
 """
 from __future__ import annotations
