@@ -97,83 +97,97 @@ struct BlockWork {
 };
 
 // Work items are numbered head-major over the exact query tiles (BQ queries) of
-// every sequence (longest sequence first within a head) and remapped so that
-// each XCD -- the dispatcher deals blocks round-robin over the 8 XCDs, so an
-// XCD receives a contiguous range of items -- gets whole heads with all their
-// sequences (balanced), and its concurrent blocks share one head's K/V in L2.
-// Blocks past the real total (the grid is sized for num_seqs x the longest
-// sequence) are dealt last and get false. cu_q NULL: dense sequences of max_q
-// queries and max_k keys. Every decoded value is wave-uniform.
-__device__ __forceinline__ bool decode_block(const int32_t* cu_q, const int32_t* cu_k, int num_seqs, int max_q,
-                                             int max_k, int heads, int nqt, int BQ, BlockWork& w) {
-    int total, seq, qt, head;
+// every sequence (longest sequence first within a head). cu_q NULL: dense
+// sequences of max_q queries. Returns the number of items (wave-uniform).
+__device__ __forceinline__ int items_total(const int32_t* cu_q, int num_seqs, int heads, int nqt, int BQ) {
+    if (cu_q == nullptr) return nqt * heads * num_seqs;   // the one-block-per-item launch's grid
+    int total = 0;
+    for (int s = 0; s < num_seqs; ++s) {
+        const int ls = __builtin_amdgcn_readfirstlane(cu_q[s + 1] - cu_q[s]);
+        total += (ls + BQ - 1) / BQ;
+    }
+    return total * heads;
+}
+
+// The items dealt to XCD x: [start, start + len). The dispatcher deals blocks
+// round-robin over the 8 XCDs, so an XCD receives every 8th block; giving it a
+// contiguous range of items hands it whole heads with all their sequences
+// (balanced), and its concurrent blocks share one head's K/V in its L2.
+__device__ __forceinline__ void xcd_slice(int total, int x, int& start, int& len) {
+    const int per = total / 8, rem = total % 8;
+    len = per + (x < rem ? 1 : 0);
+    start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+}
+
+// Item w -> (head, sequence, query tile) and the sequence's rows. Every decoded
+// value is wave-uniform.
+__device__ __forceinline__ void decode_item(int w, const int32_t* cu_q, const int32_t* cu_k, int num_seqs, int max_q,
+                                            int max_k, int nqt, int BQ, int total, int heads, BlockWork& bw) {
+    int seq, qt, head;
     int64_t s0, k0;   // first query row / first key row of the sequence
     int len, klen;    // its queries / keys
     if (cu_q == nullptr) {
-        total = nqt * heads * num_seqs;   // the launch's grid
+        const int per_head = nqt * num_seqs;
+        head = __builtin_amdgcn_readfirstlane(w / per_head);
+        const int r = w - head * per_head;
+        seq = __builtin_amdgcn_readfirstlane(r / nqt);
+        qt = __builtin_amdgcn_readfirstlane(r - seq * nqt);
+        s0 = (int64_t)seq * max_q;
+        len = max_q;
+        k0 = (int64_t)seq * max_k;
+        klen = max_k;
     } else {
-        total = 0;
-        for (int s = 0; s < num_seqs; ++s) {
-            const int ls = __builtin_amdgcn_readfirstlane(cu_q[s + 1] - cu_q[s]);
-            total += (ls + BQ - 1) / BQ;
+        const int per_head = total / heads;
+        head = __builtin_amdgcn_readfirstlane(w / per_head);
+        int r = __builtin_amdgcn_readfirstlane(w - head * per_head);
+        // walk the sequences longest first (by queries; ties: lower index first);
+        // num_seqs is small, so the O(n^2) rank walk is a handful of scalar steps
+        seq = -1;
+        qt = 0;
+        int prev_len = 0x7fffffff, prev_idx = -1;
+        for (int k = 0; k < num_seqs && seq < 0; ++k) {
+            // next sequence in (length desc, index asc) order after (prev_len, prev_idx)
+            int best = -1, best_len = -1;
+            for (int s = 0; s < num_seqs; ++s) {
+                const int ls = __builtin_amdgcn_readfirstlane(cu_q[s + 1] - cu_q[s]);
+                const bool after = num_seqs > 32 ? s > prev_idx   // many sequences: index order
+                                                   : ls < prev_len || (ls == prev_len && s > prev_idx);
+                if (after && (num_seqs > 32 ? best < 0 : ls > best_len)) { best = s; best_len = ls; }
+            }
+            const int nt = (best_len + BQ - 1) / BQ;
+            if (r < nt) { seq = best; qt = r; } else { r -= nt; prev_len = best_len; prev_idx = best; }
         }
-        total *= heads;
+        seq = __builtin_amdgcn_readfirstlane(seq);
+        qt = __builtin_amdgcn_readfirstlane(qt);
+        const int c0 = __builtin_amdgcn_readfirstlane(cu_q[seq]);
+        const int c1 = __builtin_amdgcn_readfirstlane(cu_q[seq + 1]);
+        s0 = c0;
+        len = c1 - c0;
+        const int d0 = __builtin_amdgcn_readfirstlane(cu_k[seq]);
+        const int d1 = __builtin_amdgcn_readfirstlane(cu_k[seq + 1]);
+        k0 = d0;
+        klen = d1 - d0;
     }
+    bw.head = head;
+    bw.seq = seq;
+    bw.qt = qt;
+    bw.s0 = s0;
+    bw.k0 = k0;
+    bw.len = len;
+    bw.klen = klen;
+}
+
+// One block per item: block b -> item, remapped so that consecutive items land on
+// the same XCD (xcd_slice). Blocks past the real total (the grid is sized for
+// num_seqs x the longest sequence) are dealt last and get false.
+__device__ __forceinline__ bool decode_block(const int32_t* cu_q, const int32_t* cu_k, int num_seqs, int max_q,
+                                             int max_k, int heads, int nqt, int BQ, BlockWork& w) {
+    const int total = items_total(cu_q, num_seqs, heads, nqt, BQ);
     const int b = (int)block_index();
     if (b >= total) return false;
-    {
-        const int per = total / 8, rem = total % 8;
-        const int xcd = b % 8, idx = b / 8;
-        const int w = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-        if (cu_q == nullptr) {
-            const int per_head = nqt * num_seqs;
-            head = __builtin_amdgcn_readfirstlane(w / per_head);
-            const int r = w - head * per_head;
-            seq = __builtin_amdgcn_readfirstlane(r / nqt);
-            qt = __builtin_amdgcn_readfirstlane(r - seq * nqt);
-            s0 = (int64_t)seq * max_q;
-            len = max_q;
-            k0 = (int64_t)seq * max_k;
-            klen = max_k;
-        } else {
-            const int per_head = total / heads;
-            head = __builtin_amdgcn_readfirstlane(w / per_head);
-            int r = __builtin_amdgcn_readfirstlane(w - head * per_head);
-            // walk the sequences longest first (by queries; ties: lower index first);
-            // num_seqs is small, so the O(n^2) rank walk is a handful of scalar steps
-            seq = -1;
-            int prev_len = 0x7fffffff, prev_idx = -1;
-            for (int k = 0; k < num_seqs && seq < 0; ++k) {
-                // next sequence in (length desc, index asc) order after (prev_len, prev_idx)
-                int best = -1, best_len = -1;
-                for (int s = 0; s < num_seqs; ++s) {
-                    const int ls = __builtin_amdgcn_readfirstlane(cu_q[s + 1] - cu_q[s]);
-                    const bool after = num_seqs > 32 ? s > prev_idx   // many sequences: index order
-                                                       : ls < prev_len || (ls == prev_len && s > prev_idx);
-                    if (after && (num_seqs > 32 ? best < 0 : ls > best_len)) { best = s; best_len = ls; }
-                }
-                const int nt = (best_len + BQ - 1) / BQ;
-                if (r < nt) { seq = best; qt = r; } else { r -= nt; prev_len = best_len; prev_idx = best; }
-            }
-            seq = __builtin_amdgcn_readfirstlane(seq);
-            qt = __builtin_amdgcn_readfirstlane(qt);
-            const int c0 = __builtin_amdgcn_readfirstlane(cu_q[seq]);
-            const int c1 = __builtin_amdgcn_readfirstlane(cu_q[seq + 1]);
-            s0 = c0;
-            len = c1 - c0;
-            const int d0 = __builtin_amdgcn_readfirstlane(cu_k[seq]);
-            const int d1 = __builtin_amdgcn_readfirstlane(cu_k[seq + 1]);
-            k0 = d0;
-            klen = d1 - d0;
-        }
-    }
-    w.head = head;
-    w.seq = seq;
-    w.qt = qt;
-    w.s0 = s0;
-    w.k0 = k0;
-    w.len = len;
-    w.klen = klen;
+    int start, len;
+    xcd_slice(total, b % 8, start, len);
+    decode_item(start + b / 8, cu_q, cu_k, num_seqs, max_q, max_k, nqt, BQ, total, heads, w);
     return true;
 }
 

@@ -43,6 +43,8 @@
 //     the sequence are clamped on load and never stored.
 #include <math.h>
 
+#include <atomic>
+
 #include "dit_attn_common.hpp"
 #include "dit_device.hpp"
 #include "dit_internal.h"
@@ -468,27 +470,22 @@ __device__ __forceinline__ void pipe_last(Pipe<HD, NW, QB>& p, const f32x16 (&S)
     rowsum_tile<HD, NW, QB>(p, P);
 }
 
-// QB = query blocks of 32 per wave. QB = 2 halves the LDS operand traffic per
-// flop but needs about 450 registers, i.e. one wave per SIMD (VGPRs + AGPRs);
-// QB = 1 runs two waves per SIMD.
+// One work item: the BQ = 32 QB NW queries of query tile bw.qt of one (sequence,
+// head) against all of the sequence's keys, through the block's K / V tile rings
+// in LDS. QB = query blocks of 32 per wave. QB = 2 halves the LDS operand traffic
+// per flop but needs about 450 registers, i.e. one wave per SIMD (VGPRs + AGPRs);
+// QB = 1 runs two waves per SIMD. tid: the thread's index in the block.
 template <int HD, int NW, int QB>
-__global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf16_kernel(AttnArgs a, int nqt) {
+__device__ __forceinline__ void attn_item(const AttnArgs& a, const attn::BlockWork& bw,
+                                          char (&kbuf)[Cfg<HD, NW>::ST][Cfg<HD, NW>::TILEB],
+                                          char (&vbuf)[Cfg<HD, NW>::ST][Cfg<HD, NW>::TILEB], int tid) {
     using C = Cfg<HD, NW>;
     constexpr int BQ = 32 * QB * NW;   // queries per block
-    __shared__ __attribute__((aligned(1024))) char kbuf[C::ST][C::TILEB];
-    __shared__ __attribute__((aligned(1024))) char vbuf[C::ST][C::TILEB];
-
-    // ---- block -> (head, sequence, query tile), XCD-aware (decode_block)
-    attn::BlockWork bw;
-    if (!attn::decode_block(a.cu_seqlens, a.cu_seqlens_k, a.num_seqs, a.max_seqlen, a.max_seqlen_k, a.heads, nqt,
-                            BQ, bw))
-        return;
     const int head = bw.head, qt = bw.qt, len = bw.len, klen = bw.klen;
     const int64_t s0 = bw.s0, k0 = bw.k0;
     const int q0 = qt * BQ;
     if (q0 >= len) return;
     if (klen == 0) {   // no keys: o = 0, lse = -inf (the empty sum)
-        const int tid = thread_index();
         for (int i = tid; i < BQ; i += 64 * NW) {
             const int qi = q0 + i;
             if (qi >= len) break;
@@ -502,7 +499,6 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     }
 
     Pipe<HD, NW, QB> p;
-    const int tid = thread_index();
     p.lane = tid & 63;
     p.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     p.g = p.lane >> 5;
@@ -641,14 +637,155 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     }
 }
 
+// One block per work item (the grid covers num_seqs x the longest sequence's
+// query tiles; blocks past the real items exit).
+template <int HD, int NW, int QB>
+__global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf16_kernel(AttnArgs a, int nqt) {
+    using C = Cfg<HD, NW>;
+    __shared__ __attribute__((aligned(1024))) char kbuf[C::ST][C::TILEB];
+    __shared__ __attribute__((aligned(1024))) char vbuf[C::ST][C::TILEB];
+    attn::BlockWork bw;
+    if (!attn::decode_block(a.cu_seqlens, a.cu_seqlens_k, a.num_seqs, a.max_seqlen, a.max_seqlen_k, a.heads, nqt,
+                            32 * QB * NW, bw))
+        return;
+    attn_item<HD, NW, QB>(a, bw, kbuf, vbuf, thread_index());
+}
+
+// ---- Persistent launch: one block per resident slot (CU), looping over items.
+// The XCDs of one chip run at different clocks under this load (their blocks'
+// key loops differed by up to 10% in one launch), so a fixed 1/8 of the items per
+// XCD leaves the fast XCDs idle at the end. Here every XCD draws items from its
+// own queue -- its xcd_slice range, in order, so that its concurrent blocks still
+// share a head's K/V in its L2 -- and, once that is empty, from the other XCDs'
+// queues. Each queue is an item counter in device memory (device-scope atomics);
+// the last block to finish clears the counters for the next launch that uses the
+// same slot. Launches rotate over kQueueSlots slots, so concurrently running
+// launches (other streams) use different counters as long as fewer than
+// kQueueSlots are in flight on one device.
+constexpr int kQueueSlots = 64;
+constexpr int kQWords = 16;   // one 64-byte line per counter
+__device__ uint32_t g_attn_queue[kQueueSlots][9 * kQWords];   // 8 XCD queues, then the finished-block count
+
+struct AttnLaunch {
+    AttnArgs a;
+    int nqt, nblocks;
+    uint32_t* queue;   // this launch's slot of g_attn_queue
+};
+
+// The next item for a block on XCD x: its own queue first, then the others in turn;
+// -1 when every queue is empty. Counters may run past their range (harmless).
+__device__ __forceinline__ int next_item(uint32_t* q, int total, int x) {
+    for (int t = 0; t < 8; ++t) {
+        const int v = (x + t) & 7;
+        int start, len;
+        attn::xcd_slice(total, v, start, len);
+        if (len == 0) continue;
+        const uint32_t i = atomicAdd(&q[v * kQWords], 1u);
+        if (i < (uint32_t)len) return start + (int)i;
+    }
+    return -1;
+}
+
+template <int HD, int NW, int QB>
+__global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf16_persistent(AttnLaunch L) {
+    using C = Cfg<HD, NW>;
+    constexpr int BQ = 32 * QB * NW;
+    __shared__ __attribute__((aligned(1024))) char kbuf[C::ST][C::TILEB];
+    __shared__ __attribute__((aligned(1024))) char vbuf[C::ST][C::TILEB];
+    __shared__ int s_item;
+    typedef __attribute__((address_space(4))) const AttnLaunch* kernarg_ptr;   // constant memory: scalar loads
+
+    const int total = attn::items_total(L.a.cu_seqlens, L.a.num_seqs, L.a.heads, L.nqt, BQ);
+    const int xcc = (int)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (31 << 11)) & 7);   // HW_REG_XCC_ID
+    for (;;) {
+        // The launch arguments, the item count and the thread index are redefined
+        // here for every item (empty asm, no instruction; the pointer is read back
+        // through readfirstlane, since asm outputs count as divergent): otherwise
+        // they and everything derived from them are computed once and held in
+        // registers through every key loop, where the scalar registers are already
+        // all in use.
+        uint64_t lpv = reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
+        int tt = total, tid = thread_index();
+        asm volatile("" : "+s"(lpv), "+s"(tt), "+v"(tid));
+        lpv = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(lpv >> 32)) << 32) |
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)lpv);
+        tt = __builtin_amdgcn_readfirstlane(tt);
+        const kernarg_ptr lp = (kernarg_ptr)lpv;
+        AttnArgs a;
+        a.o = lp->a.o; a.q = lp->a.q; a.k = lp->a.k; a.v = lp->a.v;
+        a.tokens = lp->a.tokens; a.heads = lp->a.heads; a.head_dim = lp->a.head_dim;
+        a.cu_seqlens = lp->a.cu_seqlens; a.num_seqs = lp->a.num_seqs; a.max_seqlen = lp->a.max_seqlen;
+        a.scale_log2 = lp->a.scale_log2; a.scale = lp->a.scale;
+        a.cu_seqlens_k = lp->a.cu_seqlens_k; a.max_seqlen_k = lp->a.max_seqlen_k; a.lse = lp->a.lse;
+
+        __syncthreads();   // the previous item's LDS reads, and every wave's read of s_item, are done
+        if (tid == 0) s_item = next_item(lp->queue, tt, xcc);
+        __syncthreads();
+        const int w = __builtin_amdgcn_readfirstlane(s_item);
+        if (w < 0) break;
+        attn::BlockWork bw;
+        attn::decode_item(w, a.cu_seqlens, a.cu_seqlens_k, a.num_seqs, a.max_seqlen, a.max_seqlen_k, lp->nqt, BQ, tt,
+                          a.heads, bw);
+        attn_item<HD, NW, QB>(a, bw, kbuf, vbuf, tid);
+    }
+    // the last block to finish clears this slot's counters for its next launch
+    if (thread_index() == 0) {
+        uint32_t* q = L.queue;
+        __threadfence();
+        if (atomicAdd(&q[8 * kQWords], 1u) == (uint32_t)(L.nblocks - 1))
+            for (int i = 0; i < 9; ++i) __hip_atomic_store(&q[i * kQWords], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Per device: compute units and the address of the queue counters.
+struct DeviceInfo {
+    std::atomic<int> cus{0};
+    std::atomic<uint32_t*> queue{nullptr};
+    std::atomic<uint32_t> next_slot{0};
+};
+DeviceInfo g_dev_info[64];
+
+hipError_t device_info(int& cus, uint32_t*& queue_slot) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    DeviceInfo& d = g_dev_info[dev];
+    int n = d.cus.load(std::memory_order_relaxed);
+    uint32_t* q = d.queue.load(std::memory_order_relaxed);
+    if (n == 0 || q == nullptr) {
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        // the array's device address (its name in host code is not that address)
+        e = hipGetSymbolAddress(reinterpret_cast<void**>(&q), HIP_SYMBOL(g_attn_queue));
+        if (e != hipSuccess) return e;
+        d.cus.store(n, std::memory_order_relaxed);
+        d.queue.store(q, std::memory_order_relaxed);
+    }
+    cus = n;
+    queue_slot = q + (size_t)(d.next_slot.fetch_add(1, std::memory_order_relaxed) % kQueueSlots) * 9 * kQWords;
+    return hipSuccess;
+}
+
 template <int HD, int NW, int QB>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     constexpr int BQ = 32 * QB * NW;
     const int nqt = (a.max_seqlen + BQ - 1) / BQ;
-    const int64_t total = (int64_t)nqt * a.heads * a.num_seqs;
-    if (total <= 0) return hipSuccess;
-    if (total > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, QB>), dim3((unsigned)total), dim3(64 * NW), 0, s, a, nqt);
+    const int64_t grid = (int64_t)nqt * a.heads * a.num_seqs;   // >= the number of items
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    int cus = 0;
+    uint32_t* queue = nullptr;
+    hipError_t e = device_info(cus, queue);
+    if (e != hipSuccess) return e;
+    const int64_t resident = (int64_t)cus * ((QB == 1 && NW == 4) ? 2 : 1);   // blocks the chip holds at once
+    if (grid >= 4 * resident && resident >= 8) {
+        // enough items per resident block for the queues to even out the XCDs
+        const AttnLaunch L{a, nqt, (int)resident, queue};
+        hipLaunchKernelGGL((attn_bf16_persistent<HD, NW, QB>), dim3((unsigned)resident), dim3(64 * NW), 0, s, L);
+    } else {
+        hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, QB>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a, nqt);
+    }
     return hipGetLastError();
 }
 

@@ -90,6 +90,50 @@ def test_full_size_sampled_rows(w):
     _check(w, rows=sample_rows(w, per_seq=48 if w.tokens > 10000 else 128))
 
 
+# Launches with at least 4 work items per resident block take the persistent
+# path (one block per compute unit, items drawn from per-XCD queues); smaller
+# ones run one block per item. Every item is computed by the same code either
+# way, so a sequence's output cannot depend on which path ran it.
+PERSISTENT = [(128, 16), (64, 32)]   # (head_dim, heads): packed (8192, 300) takes the persistent path
+
+
+@pytest.mark.parametrize("hd,heads", PERSISTENT, ids=[f"hd{hd}" for hd, _ in PERSISTENT])
+def test_persistent_launch_sampled_rows(hd, heads):
+    w = _seq_workload(f"pers{hd}", "bf16", (8192, 300), heads, hd)
+    _check(w, rows=sample_rows(w, per_seq=64))
+
+
+@pytest.mark.parametrize("hd,heads", PERSISTENT, ids=[f"hd{hd}" for hd, _ in PERSISTENT])
+def test_persistent_equals_per_item_launch(hd, heads):
+    """The 300-token sequence of the persistent launch above, bit for bit the
+    same as that sequence attended alone (a one-block-per-item launch)."""
+    need_gpu()
+    big = _seq_workload(f"pers{hd}", "bf16", (8192, 300), heads, hd)
+    inp = synth.make(big, ["q", "k", "v"])
+    got_big = _run(big, inp)
+    small = _seq_workload(f"pers{hd}_tail", "bf16", (300,), heads, hd)
+    got_small = _run(small, {n: inp[n][8192:] for n in ("q", "k", "v")})
+    assert np.array_equal(got_big[8192:], got_small)
+
+
+def test_persistent_queue_slots_reused():
+    """More persistent launches in a row than there are queue-counter slots (each
+    launch's last block clears its slot for the next launch that uses it):
+    every launch gives the same output, bit for bit."""
+    need_gpu()
+    w = _seq_workload("pers_slots", "bf16", (8192, 300), 16, 128)
+    inp = synth.make(w, ["q", "k", "v"])
+    q, k, v = (dev(inp[n], w) for n in ("q", "k", "v"))
+    cu = torch.from_numpy(w.cu_seqlens).cuda()
+    ref = torch.empty_like(q)
+    dit.dit_attn3d(ref, q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen)
+    o = torch.empty_like(q)
+    for i in range(140):
+        o.fill_(0.0)
+        dit.dit_attn3d(o, q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen)
+        assert torch.equal(o, ref), i
+
+
 def test_ulysses_share_shape():
     """One GPU's share of the 480P video workload under head-sharded context
     parallelism over 8 GPUs: 5 heads x 32,760 tokens."""
