@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace dit {
 namespace attn {
 
@@ -189,6 +191,87 @@ __device__ __forceinline__ bool decode_block(const int32_t* cu_q, const int32_t*
     xcd_slice(total, b % 8, start, len);
     decode_item(start + b / 8, cu_q, cu_k, num_seqs, max_q, max_k, nqt, BQ, total, heads, w);
     return true;
+}
+
+// ---- Persistent launches: one block per resident slot (CU), looping over items.
+// The XCDs of one chip run at different clocks under this load (their blocks'
+// key loops differed by up to 10% within one launch), so a fixed 1/8 of the items
+// per XCD leaves the fast XCDs idle at the end. In a persistent launch every XCD
+// draws items from its own queue -- its xcd_slice range, in order, so that its
+// concurrent blocks still share a head's K/V in its L2 -- and, once that is
+// empty, from the other XCDs' queues. A queue is an item counter in device memory
+// (device-scope atomics); the last block to finish clears the counters for the
+// next launch that uses the same slot. Launches rotate over kQueueSlots slots, so
+// concurrently running launches (other streams) use different counters as long
+// as fewer than kQueueSlots of one kernel file are in flight on one device. The
+// counters are per translation unit (anonymous namespace): each attention kernel
+// file has its own.
+constexpr int kQueueSlots = 64;
+constexpr int kQWords = 16;   // one 64-byte line per counter
+
+namespace {
+
+__device__ uint32_t g_attn_queue[kQueueSlots][9 * kQWords];   // 8 XCD queues, then the finished-block count
+
+// Per device: compute units, the counters' device address, the next slot.
+struct QueueDevice {
+    std::atomic<int> cus{0};
+    std::atomic<uint32_t*> queue{nullptr};
+    std::atomic<uint32_t> next_slot{0};
+};
+QueueDevice g_queue_dev[64];
+
+// Host: the current device's compute-unit count and a queue slot for one launch.
+inline hipError_t queue_launch_info(int& cus, uint32_t*& queue_slot) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    QueueDevice& d = g_queue_dev[dev];
+    int n = d.cus.load(std::memory_order_relaxed);
+    uint32_t* q = d.queue.load(std::memory_order_relaxed);
+    if (n == 0 || q == nullptr) {
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        // the array's device address on this device (its name in host code is not it)
+        e = hipGetSymbolAddress(reinterpret_cast<void**>(&q), HIP_SYMBOL(g_attn_queue));
+        if (e != hipSuccess) return e;
+        d.cus.store(n, std::memory_order_relaxed);
+        d.queue.store(q, std::memory_order_relaxed);
+    }
+    cus = n;
+    queue_slot = q + (size_t)(d.next_slot.fetch_add(1, std::memory_order_relaxed) % kQueueSlots) * 9 * kQWords;
+    return hipSuccess;
+}
+
+}  // namespace
+
+// The XCD this wave runs on (HW_REG_XCC_ID).
+__device__ __forceinline__ int xcc_id() {
+    return (int)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (31 << 11)) & 7);
+}
+
+// The next item for a block on XCD x: its own queue first, then the others in
+// turn; -1 when every queue is empty. Counters may run past their range
+// (harmless: they are cleared at the end of the launch).
+__device__ __forceinline__ int next_item(uint32_t* q, int total, int x) {
+    for (int t = 0; t < 8; ++t) {
+        const int v = (x + t) & 7;
+        int start, len;
+        xcd_slice(total, v, start, len);
+        if (len == 0) continue;
+        const uint32_t i = atomicAdd(&q[v * kQWords], 1u);
+        if (i < (uint32_t)len) return start + (int)i;
+    }
+    return -1;
+}
+
+// Called once per block (one thread) after its last item: the last block of the
+// launch clears the slot's counters.
+__device__ __forceinline__ void queue_finish(uint32_t* q, int nblocks) {
+    __threadfence();
+    if (atomicAdd(&q[8 * kQWords], 1u) == (uint32_t)(nblocks - 1))
+        for (int i = 0; i < 9; ++i) __hip_atomic_store(&q[i * kQWords], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace attn

@@ -43,8 +43,6 @@
 //     the sequence are clamped on load and never stored.
 #include <math.h>
 
-#include <atomic>
-
 #include "dit_attn_common.hpp"
 #include "dit_device.hpp"
 #include "dit_internal.h"
@@ -651,40 +649,12 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     attn_item<HD, NW, QB>(a, bw, kbuf, vbuf, thread_index());
 }
 
-// ---- Persistent launch: one block per resident slot (CU), looping over items.
-// The XCDs of one chip run at different clocks under this load (their blocks'
-// key loops differed by up to 10% in one launch), so a fixed 1/8 of the items per
-// XCD leaves the fast XCDs idle at the end. Here every XCD draws items from its
-// own queue -- its xcd_slice range, in order, so that its concurrent blocks still
-// share a head's K/V in its L2 -- and, once that is empty, from the other XCDs'
-// queues. Each queue is an item counter in device memory (device-scope atomics);
-// the last block to finish clears the counters for the next launch that uses the
-// same slot. Launches rotate over kQueueSlots slots, so concurrently running
-// launches (other streams) use different counters as long as fewer than
-// kQueueSlots are in flight on one device.
-constexpr int kQueueSlots = 64;
-constexpr int kQWords = 16;   // one 64-byte line per counter
-__device__ uint32_t g_attn_queue[kQueueSlots][9 * kQWords];   // 8 XCD queues, then the finished-block count
-
+// ---- Persistent launch (work queues: dit_attn_common.hpp)
 struct AttnLaunch {
     AttnArgs a;
     int nqt, nblocks;
     uint32_t* queue;   // this launch's slot of g_attn_queue
 };
-
-// The next item for a block on XCD x: its own queue first, then the others in turn;
-// -1 when every queue is empty. Counters may run past their range (harmless).
-__device__ __forceinline__ int next_item(uint32_t* q, int total, int x) {
-    for (int t = 0; t < 8; ++t) {
-        const int v = (x + t) & 7;
-        int start, len;
-        attn::xcd_slice(total, v, start, len);
-        if (len == 0) continue;
-        const uint32_t i = atomicAdd(&q[v * kQWords], 1u);
-        if (i < (uint32_t)len) return start + (int)i;
-    }
-    return -1;
-}
 
 template <int HD, int NW, int QB>
 __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf16_persistent(AttnLaunch L) {
@@ -696,7 +666,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     typedef __attribute__((address_space(4))) const AttnLaunch* kernarg_ptr;   // constant memory: scalar loads
 
     const int total = attn::items_total(L.a.cu_seqlens, L.a.num_seqs, L.a.heads, L.nqt, BQ);
-    const int xcc = (int)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (31 << 11)) & 7);   // HW_REG_XCC_ID
+    const int xcc = attn::xcc_id();
     for (;;) {
         // The launch arguments, the item count and the thread index are redefined
         // here for every item (empty asm, no instruction; the pointer is read back
@@ -719,7 +689,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
         a.cu_seqlens_k = lp->a.cu_seqlens_k; a.max_seqlen_k = lp->a.max_seqlen_k; a.lse = lp->a.lse;
 
         __syncthreads();   // the previous item's LDS reads, and every wave's read of s_item, are done
-        if (tid == 0) s_item = next_item(lp->queue, tt, xcc);
+        if (tid == 0) s_item = attn::next_item(lp->queue, tt, xcc);
         __syncthreads();
         const int w = __builtin_amdgcn_readfirstlane(s_item);
         if (w < 0) break;
@@ -730,41 +700,8 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     }
     // the last block to finish clears this slot's counters for its next launch
     if (thread_index() == 0) {
-        uint32_t* q = L.queue;
-        __threadfence();
-        if (atomicAdd(&q[8 * kQWords], 1u) == (uint32_t)(L.nblocks - 1))
-            for (int i = 0; i < 9; ++i) __hip_atomic_store(&q[i * kQWords], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        attn::queue_finish(L.queue, L.nblocks);
     }
-}
-
-// Per device: compute units and the address of the queue counters.
-struct DeviceInfo {
-    std::atomic<int> cus{0};
-    std::atomic<uint32_t*> queue{nullptr};
-    std::atomic<uint32_t> next_slot{0};
-};
-DeviceInfo g_dev_info[64];
-
-hipError_t device_info(int& cus, uint32_t*& queue_slot) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    DeviceInfo& d = g_dev_info[dev];
-    int n = d.cus.load(std::memory_order_relaxed);
-    uint32_t* q = d.queue.load(std::memory_order_relaxed);
-    if (n == 0 || q == nullptr) {
-        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        // the array's device address (its name in host code is not that address)
-        e = hipGetSymbolAddress(reinterpret_cast<void**>(&q), HIP_SYMBOL(g_attn_queue));
-        if (e != hipSuccess) return e;
-        d.cus.store(n, std::memory_order_relaxed);
-        d.queue.store(q, std::memory_order_relaxed);
-    }
-    cus = n;
-    queue_slot = q + (size_t)(d.next_slot.fetch_add(1, std::memory_order_relaxed) % kQueueSlots) * 9 * kQWords;
-    return hipSuccess;
 }
 
 template <int HD, int NW, int QB>
@@ -776,7 +713,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     int cus = 0;
     uint32_t* queue = nullptr;
-    hipError_t e = device_info(cus, queue);
+    hipError_t e = attn::queue_launch_info(cus, queue);
     if (e != hipSuccess) return e;
     const int64_t resident = (int64_t)cus * ((QB == 1 && NW == 4) ? 2 : 1);   // blocks the chip holds at once
     if (grid >= 4 * resident && resident >= 8) {
