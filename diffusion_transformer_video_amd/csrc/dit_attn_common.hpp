@@ -221,8 +221,9 @@ struct QueueDevice {
 };
 QueueDevice g_queue_dev[64];
 
-// Host: the current device's compute-unit count and a queue slot for one launch.
-inline hipError_t queue_launch_info(int& cus, uint32_t*& queue_slot) {
+// Host: the current device's compute-unit count and, when want_slot, a queue
+// slot for one launch.
+inline hipError_t queue_launch_info(int& cus, uint32_t*& queue_slot, bool want_slot) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -240,7 +241,9 @@ inline hipError_t queue_launch_info(int& cus, uint32_t*& queue_slot) {
         d.queue.store(q, std::memory_order_relaxed);
     }
     cus = n;
-    queue_slot = q + (size_t)(d.next_slot.fetch_add(1, std::memory_order_relaxed) % kQueueSlots) * 9 * kQWords;
+    queue_slot = want_slot
+                     ? q + (size_t)(d.next_slot.fetch_add(1, std::memory_order_relaxed) % kQueueSlots) * 9 * kQWords
+                     : nullptr;
     return hipSuccess;
 }
 

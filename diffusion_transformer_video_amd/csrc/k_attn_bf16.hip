@@ -713,11 +713,13 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     int cus = 0;
     uint32_t* queue = nullptr;
-    hipError_t e = attn::queue_launch_info(cus, queue);
+    hipError_t e = attn::queue_launch_info(cus, queue, false);
     if (e != hipSuccess) return e;
     const int64_t resident = (int64_t)cus * ((QB == 1 && NW == 4) ? 2 : 1);   // blocks the chip holds at once
     if (grid >= 4 * resident && resident >= 8) {
         // enough items per resident block for the queues to even out the XCDs
+        e = attn::queue_launch_info(cus, queue, true);
+        if (e != hipSuccess) return e;
         const AttnLaunch L{a, nqt, (int)resident, queue};
         hipLaunchKernelGGL((attn_bf16_persistent<HD, NW, QB>), dim3((unsigned)resident), dim3(64 * NW), 0, s, L);
     } else {

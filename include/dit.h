@@ -130,6 +130,11 @@ int dit_rope3d(void* q, void* k, int64_t tokens, int32_t heads, int32_t head_dim
  *   head_dim in {64, 128} (else DIT_E_UNSUPPORTED)
  * bf16 runs on MFMA with float32 accumulation; probabilities enter the second
  * product rounded to bf16. float32 runs on the vector ALUs in full float32.
+ * Large bf16 launches (at least 4 query tiles of 256 (128 at head_dim 64) per
+ * block the device holds at once) run one block per compute unit drawing work
+ * from counters in library-owned device memory: at most 64 such launches
+ * (dit_attn3d and dit_attn3d_lse together) may be in flight on one device at
+ * once, e.g. on different streams. Results do not depend on the launch form.
  */
 int dit_attn3d(void* o, const void* q, const void* k, const void* v,
                int64_t tokens, int32_t heads, int32_t head_dim,
