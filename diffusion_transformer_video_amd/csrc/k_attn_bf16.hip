@@ -41,6 +41,10 @@
 //     The row sum accumulates the bf16-rounded probabilities the product uses.
 //   * Only the last key tile of a sequence carries a mask; rows past the end of
 //     the sequence are clamped on load and never stored.
+//   * Two launch forms run the same per-item code: one block per work item, or,
+//     for grids of at least 4 items per resident block, one persistent block per
+//     compute unit drawing items from per-XCD queues with stealing (the XCDs run
+//     at different clocks under this load; see dit_attn_common.hpp).
 #include <math.h>
 
 #include "dit_attn_common.hpp"
@@ -287,24 +291,6 @@ __device__ __forceinline__ void pv_step(const uint32_t (&vb)[Cfg<HD, NW>::NDT], 
         for (int qb = 0; qb < QB; ++qb)
             O[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, P[qb][2 * KB + T], O[qb][dt], 0, 0, 0);
     }
-}
-
-template <int HD, int NW, int QB, int KB, int T>
-__device__ __forceinline__ void pv_read(const uint32_t (&vb)[Cfg<HD, NW>::NDT], bf16x8 (&v)[Cfg<HD, NW>::NDT]) {
-    using C = Cfg<HD, NW>;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) v[dt] = vt_operand<(32 * KB + 16 * T) * C::ROWB, 8 * C::ROWB>(vb[dt]);
-}
-
-template <int HD, int NW, int QB>
-__device__ __forceinline__ void pv_mfma(const bf16x8 (&v)[Cfg<HD, NW>::NDT], const bf16x8 (&P)[QB][4], int i,
-                                        f32x16 (&O)[QB][Cfg<HD, NW>::NDT]) {
-    using C = Cfg<HD, NW>;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-            O[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[dt], P[qb][i], O[qb][dt], 0, 0, 0);
 }
 
 template <int HD, int NW, int QB>
