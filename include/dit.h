@@ -37,7 +37,9 @@
  *
  * Conventions shared by every entry point:
  *   - Pointers to tensors are DEVICE pointers owned by the caller. The library
- *     allocates no device memory and keeps no per-call state.
+ *     allocates no device memory at call time. Its only device state is a fixed
+ *     array of work-queue counters, loaded with the library, that large bf16
+ *     attention launches use and leave cleared (see dit_attn3d).
  *   - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue work
  *     on it and never synchronise; results are visible after the stream is
  *     synchronised. Faults inside a running kernel surface at that sync.
