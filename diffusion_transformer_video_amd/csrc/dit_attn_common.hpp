@@ -1,6 +1,8 @@
 // Pieces shared by the gfx950 attention kernels (bf16 and fp8): lane-pair
-// reductions over the two halves of a wave, buffer loads, the direct HBM -> LDS
-// load, and the block -> (head, sequence, query tile) decode.
+// reductions over the two halves of a wave, buffer loads and range-checked
+// stores, the direct HBM -> LDS load, the numbering of work items (query tiles)
+// and their XCD-aware dealing to blocks, and the per-XCD work queues of the
+// persistent launch.
 #pragma once
 
 #include <hip/hip_runtime.h>

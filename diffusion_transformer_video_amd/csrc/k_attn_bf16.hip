@@ -30,10 +30,14 @@
 //   * Software pipeline: the K stream runs one tile ahead of V. Iteration j
 //     holds S(j) in registers and, in one straight-line block, computes the
 //     softmax of S(j) on the vector ALU while the matrix cores compute
-//     S(j+1) = K(j+1) Q^T, then O += V(j) P(j). LDS holds K(j+1), K(j+2),
-//     V(j), V(j+1) (64 KB). The loads are issued from inline asm and waited for
-//     explicitly, so the compiler never stalls a read of tile j on the loads of
-//     tile j+1 in flight. One barrier per tile.
+//     S(j+1) = K(j+1) Q^T, then O += V(j) P(j). With 8 waves the K and V tiles
+//     sit in three-slot LDS rings (96 KB): step j reads K(j+1) and V(j), K(j+2)
+//     and V(j+1) have landed, K(j+3) and V(j+2) are being loaded (with 4 waves,
+//     two-slot rings and one tile ahead). The loop is unrolled over six steps,
+//     so every ring slot offset is a compile-time constant. The loads are
+//     issued from inline asm and waited for explicitly, so the compiler never
+//     stalls a read of one tile on the loads of later tiles in flight. One
+//     barrier per tile.
 //   * Online softmax in the exp2 domain with the 1/sqrt(d) scale folded into
 //     one fma. The running max is only raised (and O, l rescaled) when a new
 //     tile maximum exceeds it by more than 2^8 -- a wave-uniform branch -- so

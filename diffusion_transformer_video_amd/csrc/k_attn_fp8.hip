@@ -25,8 +25,9 @@
 //     a tile max exceeds it by more than 2: the largest weight lies in
 //     [2^6, 2^8] (E4M3 holds up to 448), so weights down to 2^-12 of the
 //     largest keep E4M3's full 3-bit precision;
-//   * the exponentials alone take as many cycles per tile as the products (a
-//     quarter-rate instruction per score), so the vector ALU is the bound and
+//   * the exponentials alone take about as many cycles per tile as the
+//     products (one per score, each costing about two vector-ALU issue slots
+//     in a throughput probe), so the vector ALU is the bound and
 //     the rest of the softmax is kept off it: the row sums are one more
 //     product per tile, against a constant operand whose row 0 is 1.0 (they
 //     add the same E4M3 probabilities the output product uses); the tile loop
