@@ -179,7 +179,7 @@ def test_peaked_scores():
     _run_case(q, k, v, cu, 2, 500)
 
 
-@pytest.mark.parametrize("w", [synth.C2, synth.C3, synth.C5], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [synth.C2, synth.C3, synth.C4, synth.C5], ids=lambda w: w.name)
 def test_full_size_sampled_rows(w):
     need_gpu()
     (q, k, v), cu = _inputs(w)
