@@ -377,6 +377,27 @@ def main():
         kern_ms["attn_ulysses_share"] = e0.elapsed_time(e1) / 5
         ulysses_flops = 4 * 32760 ** 2 * 5 * 128
         del uq, uk, uv, uo
+        # the same workload's tokens and d_model as heads of 64 (the other head
+        # size the attention kernel supports): 2 x 4096-token sequences here
+        hsh = (w.tokens, w.heads * 2, 64)
+        hq, hk, hv = (torch.randn(hsh, device="cuda", generator=gen).to(torch.bfloat16) for _ in range(3))
+        ho = torch.empty_like(hq)
+        hd64_kw = ({"num_seqs": w.num_seqs} if cu is None else {"cu_seqlens": cu, "max_seqlen": w.max_seqlen})
+
+        def attn_hd64():
+            dit.dit_attn3d(ho, hq, hk, hv, **hd64_kw)
+        attn_hd64()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            attn_hd64()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            attn_hd64()
+        e1.record()
+        torch.cuda.synchronize()
+        kern_ms["attn_hd64"] = e0.elapsed_time(e1) / 5
+        del hq, hk, hv, ho
 
     # flow-matching training side (not part of the sampling step): the straight-path
     # interpolant and the flow-matching loss over the latent
@@ -442,6 +463,10 @@ def main():
         tu = ulysses_flops / (kern_ms["attn_ulysses_share"] * 1e-3) / 1e12
         kernels["attn_ulysses_share"] = {"us": round(kern_ms["attn_ulysses_share"] * 1e3, 2), "tflops": round(tu, 2),
                                          "shape": "32760 tokens x 5 heads x 128 (480P video, 8-way Ulysses share)"}
+    if "attn_hd64" in kern_ms:
+        kernels["attn_hd64"] = {"us": round(kern_ms["attn_hd64"] * 1e3, 2),
+                                "tflops": round(flops / (kern_ms["attn_hd64"] * 1e-3) / 1e12, 2),
+                                "shape": f"{w.tokens} tokens x {w.heads * 2} heads x 64 (the workload's d_model)"}
     if "attn_fp8" in kern_ms:
         tf8 = flops / (kern_ms["attn_fp8"] * 1e-3) / 1e12
         kernels["attn_fp8"] = {"us": round(kern_ms["attn_fp8"] * 1e3, 2), "tflops": round(tf8, 2),
