@@ -116,6 +116,17 @@ def test_persistent_equals_per_item_launch(hd, heads):
     assert np.array_equal(got_big[8192:], got_small)
 
 
+def test_persistent_launch_many_sequences():
+    """A packed batch of 40 ragged sequences (more than 32: the item numbering
+    walks them in index order) large enough for the persistent launch (2,304
+    query tiles over 12 heads), on sampled rows of every sequence."""
+    r = np.random.default_rng(17)
+    lens = tuple(int(n) for n in r.integers(1, 2400, size=40))
+    w = _seq_workload("pers_many", "bf16", lens, 12, 128)
+    assert sum(-(-n // 256) for n in lens) * 12 >= 1024
+    _check(w, rows=sample_rows(w, per_seq=8, edge=2))
+
+
 def test_persistent_queue_slots_reused():
     """More persistent launches in a row than there are queue-counter slots (each
     launch's last block clears its slot for the next launch that uses it):
