@@ -43,7 +43,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50,
+                   help="timed steps (50 attention launches bracketed by events at the default)")
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--warmup-min-s", type=float, default=0.25,
                    help="keep running untimed warmup steps (beyond --warmup) until this much wall "
