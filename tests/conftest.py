@@ -11,4 +11,4 @@ if TESTS not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-    config.addinivalue_line("markers", "slow: full-size workload parity (GPU box only)")
+    config.addinivalue_line("markers", "slow: full-size workload parity (needs a GPU)")
