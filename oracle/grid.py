@@ -56,7 +56,3 @@ def positions(cu_seqlens: np.ndarray, grid_h: int, grid_w: int) -> np.ndarray:
         return np.zeros((0, 3), dtype=np.int64)
     return np.concatenate(parts, axis=0)
 
-
-def param_row(token: np.ndarray, tokens_per_row: int) -> np.ndarray:
-    """Row of the per-sample / per-frame parameter tables used by a token."""
-    return np.asarray(token, dtype=np.int64) // int(tokens_per_row)

@@ -43,6 +43,7 @@ def real_impl():
         interpolant_rows=o_epi.interpolant_rows, cfm_loss=o_epi.cfm_loss, midpoint_half=o_epi.midpoint_half,
         insert_frames=o_flow.insert_frames, frame_schedule=o_flow.frame_schedule,
         e4m3_encode=o_fp8.e4m3_encode, e4m3_decode=o_fp8.e4m3_decode, quantize_per_head=o_fp8.quantize_per_head,
+        dequantize=o_fp8.dequantize,
     )
 
 
@@ -721,6 +722,41 @@ def pin_quantize_per_head(impl):
         assert np.all(np.abs(deq - x[:, h, :]) <= np.maximum(np.abs(x[:, h, :]) * 2.0 ** -4, 2.0 ** -10 * scale[h]) * (1 + 1e-6))
         assert amax[h] == np.abs(x[:, h, :]).max()
     assert np.all(codes[:, 2, :] == 0) and scale[2] == 1.0
+
+
+def pin_dequantize_per_head(impl):
+    """dequantize(codes, scale) gives back the quantised tensor: shape
+    [tokens, heads, d] with tokens, heads and d all different; the element of
+    largest magnitude of each head comes back as +-amax to float32 precision
+    (448 times the scale amax / 448); every element within half a code spacing
+    (relative 2^-4, or 2^-10 of the scale below E4M3's normal range) of the
+    value it came from; an all-zero head is zero. Also on hand-built codes,
+    against values listed from the format's definition: code 0x38 (1.0) gives
+    exactly the head's scale, 0x7E (448) gives 448 times it, 0xC0 (-2) minus
+    twice it, 0x01 (2^-9) 2^-9 times it."""
+    r = _rng(72)
+    mags = np.array([1.0, 30.0, 0.0, 0.01], np.float32)
+    x = r.standard_normal((40, 4, 16)).astype(np.float32) * mags[None, :, None]
+    codes, amax, scale = impl.quantize_per_head(x)
+    deq = np.asarray(impl.dequantize(codes, scale))
+    assert deq.shape == x.shape
+    for h in range(4):
+        xh = x[:, h, :].astype(np.float64)
+        dh = deq[:, h, :]
+        if mags[h] == 0:
+            assert np.all(dh == 0)
+            continue
+        i = np.unravel_index(np.argmax(np.abs(xh)), xh.shape)
+        assert abs(abs(dh[i]) - float(amax[h])) <= float(amax[h]) * 2.0 ** -23
+        assert np.sign(dh[i]) == np.sign(xh[i])
+        assert np.all(np.abs(dh - xh) <= np.maximum(np.abs(xh) * 2.0 ** -4, 2.0 ** -10 * float(scale[h])) * (1 + 1e-6))
+    sc = np.array([0.5, 3.0, 1e-3], np.float32)
+    vals = {0x38: 1.0, 0x7E: 448.0, 0xC0: -2.0, 0x01: 2.0 ** -9, 0x00: 0.0}
+    for c, v in vals.items():
+        cc = np.full((5, 3, 2), c, np.uint8)
+        got = np.asarray(impl.dequantize(cc, sc))
+        want = v * sc.astype(np.float64)[None, :, None] * np.ones((5, 3, 2))
+        assert np.array_equal(got, want), hex(c)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -7,13 +7,18 @@ Tolerance of the attention (derived from the arithmetic; checked per element):
 the only rounding between the dequantised inputs and the float32 accumulators
 is the E4M3 rounding of the probabilities before the second product. In the
 kernel's units P_k = 2^(s_k log2 e - m + 6), the largest weight lies in
-[2^6, 2^8]; rounding to nearest moves P_k by at most half its spacing: 2^-4 P_k
-for normal values, 2^-10 below 2^-6 (subnormals). Relative to the row total
-that is at most h_k = 2^-4 w_k + 2^-16 (w = the softmax weights). The row sum
-uses the unrounded P, so the output moves by sum_k d_k v_k / sum P with
-independent, zero-mean d_k in [-h_k, h_k]; its standard deviation is at most
-sigma = sqrt(sum_k h_k^2 / 3 (|v_k| + |o|)^2). Bar per element: 7 sigma (a
-Gaussian tail of ~1e-12 per element) + 2^-8 |o| (the bf16 store) + 1e-4.
+[2^6, 2^8]; rounding to nearest moves P_k by d_k, at most half its spacing:
+2^-4 P_k for normal values, 2^-10 below 2^-6 (subnormals). Relative to the row
+total L = sum P that is |d_k| / L <= h_k = 2^-4 w_k + 2^-16 (w = the softmax
+weights). The kernel's row sum adds the same rounded values the product uses
+(a product against a constant ones operand), so the output is
+sum (P_k + d_k) v_k / (L + D) with D = sum d_k, and its error is
+    sum_k d_k (v_k - o) / (L + D)  =  [sum_k (d_k / L)(v_k - o)] / (1 + D / L).
+With independent, zero-mean d_k / L in [-h_k, h_k] the numerator has standard
+deviation at most sigma = sqrt(sum_k h_k^2 / 3 (|v_k| + |o|)^2), and
+D / L has standard deviation at most sigma_D = sqrt(sum_k h_k^2 / 3). Bar per
+element: 7 sigma / (1 - 7 sigma_D) (a Gaussian tail of ~1e-12 per element for
+either sum) + 2^-8 |o| (the bf16 store) + 1e-4.
 """
 import math
 
@@ -97,7 +102,9 @@ def _fp8_bound(qd, kd, vd, cu, rows):
             # sum_k hk^2 (|v_k| + |o|)^2 = sum hk^2 v^2 + 2|o| sum hk^2 |v| + o^2 sum hk^2
             h2 = hk * hk
             var = (h2 @ (V * V) + 2 * oo * (h2 @ V) + oo * oo * h2.sum(axis=1, keepdims=True)) / 3.0
-            tol[sel, h, :] = 7.0 * np.sqrt(var) + 2.0 ** -8 * oo + 1e-4
+            sig_d = np.sqrt(h2.sum(axis=1, keepdims=True) / 3.0)              # of D / L, per row
+            assert np.all(7.0 * sig_d < 0.5)
+            tol[sel, h, :] = 7.0 * np.sqrt(var) / (1.0 - 7.0 * sig_d) + 2.0 ** -8 * oo + 1e-4
     return o, tol
 
 

@@ -190,6 +190,21 @@ def _quantize_per_tensor(x):
     return codes, np.full(h, amax, np.float32), np.full(h, amax / np.float32(448), np.float32)
 
 
+def _dequant_by_amax(codes, scale):
+    from oracle import fp8
+    return fp8.e4m3_decode(codes) * (np.asarray(scale, np.float64) * 448.0)[None, :, None]
+
+
+def _dequant_over_tokens(codes, scale):
+    from oracle import fp8
+    return fp8.e4m3_decode(codes) * np.asarray(scale, np.float64)[:, None, None]
+
+
+def _dequant_over_dims(codes, scale):
+    from oracle import fp8
+    return fp8.e4m3_decode(codes) * np.asarray(scale, np.float64)[None, None, :]
+
+
 def _coords_swapped(n, gh, gw):
     n = np.asarray(n, dtype=np.int64)
     return np.stack([n // (gh * gw), n % gw, (n // gw) % gh], axis=-1)
@@ -248,6 +263,9 @@ MUTANTS = {
     "e4m3_truncating": dict(e4m3_encode=_e4m3_truncate),
     "e4m3_bias_8": dict(e4m3_decode=_e4m3_decode_bias8),
     "fp8_scale_per_tensor": dict(quantize_per_head=_quantize_per_tensor),
+    "dequant_scale_is_amax": dict(dequantize=_dequant_by_amax),
+    "dequant_scale_over_tokens": dict(dequantize=_dequant_over_tokens),
+    "dequant_scale_over_dims": dict(dequantize=_dequant_over_dims),
     "grid_h_w_swapped": dict(coords=_coords_swapped),
     "interpolant_reversed": dict(interpolant=_interp_reversed),
     "euler_wrong_sign": dict(euler_step=_euler_minus),
