@@ -19,9 +19,8 @@ import os
 from typing import Optional, Sequence
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# DIT_LIB_PATH selects another build of the same library (e.g. an experiment);
-# by default the in-tree libdit.so next to this file is loaded
-LIB_PATH = os.environ.get("DIT_LIB_PATH") or os.path.join(_PKG, "libdit.so")
+# the in-tree build, next to this file; no other copy is ever loaded
+LIB_PATH = os.path.join(_PKG, "libdit.so")
 
 DIT_F32, DIT_BF16 = 0, 1
 DIT_OK, DIT_E_INVAL, DIT_E_UNSUPPORTED, DIT_E_HIP = 0, 1, 2, 3
@@ -131,6 +130,21 @@ def _f32(*ts) -> None:
             raise TypeError("parameter tables (gamma, beta, alpha, dt_rows) and lse / accumulators must be float32")
 
 
+def _offsets(*pairs) -> None:
+    """Sequence offsets (cu_seqlens) must be int32 [num_seqs + 1]: the kernels
+    read them as int32, so int64 offsets (torch's default integer type) would be
+    taken as pairs of int32 values. Checked before anything else, so a wrong
+    type raises before any launch."""
+    torch = _torch()
+    for name, t in pairs:
+        if t is None:
+            continue
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32, got {t.dtype}")
+        if t.dim() != 1 or t.numel() < 2:
+            raise ValueError(f"{name} must be a 1-D tensor of num_seqs + 1 >= 2 offsets")
+
+
 def _stream(stream) -> int:
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -158,7 +172,12 @@ def dit_rope3d(q, k, grid: Sequence[int], split: Sequence[int], base: float = 10
     """Rotate q and k ([tokens, heads, head_dim]) in place by R_3D(t', h', w').
 
     grid = (T', H', W'); with cu_seqlens, T' is ignored and positions restart per
-    packed sequence. split = (d_t, d_h, d_w)."""
+    packed sequence. split = (d_t, d_h, d_w). pos_out (optional): int32 with at
+    least 3 * tokens elements, receives (t', h', w') per token."""
+    torch = _torch()
+    _offsets(("cu_seqlens", cu_seqlens))
+    if pos_out is not None and (pos_out.dtype != torch.int32 or pos_out.numel() < 3 * q.shape[0]):
+        raise TypeError("pos_out must be int32 with at least 3 * tokens elements")
     _dev(q, k, cu_seqlens, pos_out)
     if q.dim() != 3 or (k is not None and (k.shape != q.shape or k.dtype != q.dtype)):
         raise ValueError("q and k must be [tokens, heads, head_dim] of one dtype")
@@ -173,7 +192,9 @@ def dit_rope3d(q, k, grid: Sequence[int], split: Sequence[int], base: float = 10
 
 
 def dit_attn3d(o, q, k, v, cu_seqlens=None, num_seqs: int = 1, max_seqlen: int = 0, stream=None):
-    """o = softmax(q k^T / sqrt(head_dim)) v per (sequence, head); all [tokens, heads, hd]."""
+    """o = softmax(q k^T / sqrt(head_dim)) v per (sequence, head); all [tokens, heads, hd].
+    cu_seqlens: None (dense, num_seqs equal sequences) or device int32 [num_seqs + 1]."""
+    _offsets(("cu_seqlens", cu_seqlens))
     _dev(o, q, k, v, cu_seqlens)
     if q.dim() != 3 or any(t.shape != q.shape or t.dtype != q.dtype for t in (k, v, o)):
         raise ValueError("o, q, k, v must be [tokens, heads, head_dim] of one dtype")
@@ -193,6 +214,9 @@ def dit_attn3d_lse(o, lse, q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, num_se
     q, o [tokens_q, heads, hd]; k, v [tokens_k, heads, hd]; lse [tokens_q, heads]
     float32 (natural log). cu_seqlens_q / cu_seqlens_k: both None (dense,
     num_seqs equal sequences) or both device int32 [num_seqs + 1]."""
+    _offsets(("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k))
+    if (cu_seqlens_q is None) != (cu_seqlens_k is None):
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be given together")
     _dev(o, lse, q, k, v, cu_seqlens_q, cu_seqlens_k)
     _f32(lse)
     if q.dim() != 3 or o.shape != q.shape or any(t.dtype != q.dtype for t in (k, v, o)):
@@ -308,6 +332,7 @@ def flow_insert_frames(z_out, t_out, cu_out, src_out, z, t_frames, cu_seqlens, c
     """Insert counts[f] noise frames right after every existing frame f of the packed
     batch z ([frames * tokens_per_frame, channels]); see include/dit.h."""
     torch = _torch()
+    _offsets(("cu_seqlens", cu_seqlens), ("cu_out", cu_out))
     _dev(z_out, t_out, cu_out, src_out, z, t_frames, cu_seqlens, counts, noise)
     _f32(t_out, t_frames)
     for t in (cu_out, src_out, cu_seqlens, counts):
@@ -351,6 +376,7 @@ def dit_quant_fp8(q8, k8, v8t, amax, q, k, v, cu_seqlens=None, num_seqs: int = 1
     """q, k, v (bf16 [tokens, heads, 128]) -> E4M3 codes q8, k8 (uint8, same shape),
     v8t (uint8 [heads, 128, v_stride]) and amax (float32 [3, heads])."""
     torch = _torch()
+    _offsets(("cu_seqlens", cu_seqlens))
     _dev(q8, k8, v8t, amax, q, k, v, cu_seqlens)
     _f32(amax)
     if any(t.dtype != torch.uint8 for t in (q8, k8, v8t)):
@@ -371,6 +397,7 @@ def dit_quant_fp8(q8, k8, v8t, amax, q, k, v, cu_seqlens=None, num_seqs: int = 1
 def dit_attn3d_fp8(o, q8, k8, v8t, amax, cu_seqlens=None, num_seqs: int = 1, max_seqlen: int = 0, stream=None):
     """o (bf16 [tokens, heads, 128]) = attention on the E4M3 codes written by dit_quant_fp8."""
     torch = _torch()
+    _offsets(("cu_seqlens", cu_seqlens))
     _dev(o, q8, k8, v8t, amax, cu_seqlens)
     _f32(amax)
     if o.dtype != torch.bfloat16 or o.dim() != 3 or q8.shape != o.shape or k8.shape != o.shape:

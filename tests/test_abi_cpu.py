@@ -222,3 +222,34 @@ def test_binding_raises_without_gpu_tensors():
     x = torch.zeros(4, 8)
     with pytest.raises(ValueError):
         dit.rf_euler_step(x, x, x, torch.zeros(1), 4)
+
+
+def test_binding_rejects_int64_offsets_before_any_launch():
+    """Sequence offsets must be int32: an int64 tensor (torch's default integer
+    type) would be read as pairs of int32 values. The binding raises TypeError
+    before the device check and before any call into the library."""
+    import torch
+    q = torch.zeros(8, 2, 64)
+    cu64 = torch.tensor([0, 3, 8], dtype=torch.int64)
+    with pytest.raises(TypeError):
+        dit.dit_attn3d(q, q, q, q, cu_seqlens=cu64, max_seqlen=5)
+    with pytest.raises(TypeError):
+        dit.dit_attn3d_lse(q, torch.zeros(8, 2), q, q, q, cu64, cu64, max_seqlen_q=5, max_seqlen_k=5)
+    with pytest.raises(TypeError):
+        dit.dit_rope3d(q, q, (1, 1, 8), (0, 32, 32), cu_seqlens=cu64)
+    with pytest.raises(TypeError):
+        dit.dit_quant_fp8(q, q, q, q, q, q, q, cu_seqlens=cu64, max_seqlen=5)
+    with pytest.raises(TypeError):
+        dit.dit_attn3d_fp8(q, q, q, q, q, cu_seqlens=cu64, max_seqlen=5)
+    # pos_out: int32 with room for (t', h', w') of every token
+    with pytest.raises(TypeError):
+        dit.dit_rope3d(q, q, (1, 1, 8), (0, 32, 32), pos_out=torch.zeros(24, dtype=torch.int64))
+    with pytest.raises(TypeError):
+        dit.dit_rope3d(q, q, (1, 1, 8), (0, 32, 32), pos_out=torch.zeros(23, dtype=torch.int32))
+
+
+def test_binding_loads_the_in_tree_library():
+    """The binding loads only the libdit.so built next to it."""
+    pkg = os.path.dirname(os.path.abspath(dit.__file__))
+    assert dit.LIB_PATH == os.path.join(pkg, "libdit.so")
+    assert dit.lib()._name == dit.LIB_PATH
