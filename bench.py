@@ -4,9 +4,9 @@
 One step = one pass of the whole path over one batch of synthetic input:
   dit_adaln_modulate (x -> y), dit_rope3d (q, k in place), dit_attn3d (q, k, v -> o),
   dit_gated_residual fused with the rectified-flow Euler update (x + alpha*o, z + dt*u).
-Inputs are seeded synthetic tensors shaped like the pages' image latent (default:
-128x128x16 latent, patch 2x2 -> 4096 tokens, batch 2, 24 heads x 128), resident in
-HBM before timing starts.
+Inputs are seeded synthetic tensors shaped like the pages' video latents (default:
+the 480P latent T=21, H=60, W=104, patch 1x2x2 -> 32,760 tokens, 40 heads x 128,
+3D-RoPE 44/42/42), resident in HBM before timing starts.
 
 Prints ONE JSON line. value = attention FLOPs per step / wall time per step
 (whole path), in TFLOP/s. roofline = the attention kernel's own rate, timed with
@@ -46,11 +46,13 @@ def parse():
     p.add_argument("--steps", type=int, default=50,
                    help="timed steps (50 attention launches bracketed by events at the default)")
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--warmup-min-s", type=float, default=0.25,
-                   help="keep running untimed warmup steps (beyond --warmup) until this much wall "
-                        "time has passed: an idle MI355X needs about 40 ms of load to reach its "
-                        "sustained clocks, longer than a few steps of the small workloads")
-    p.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_KEYS))
+    p.add_argument("--warmup-min-s", type=float, default=0.0,
+                   help="optional floor: keep running untimed warmup steps beyond --warmup until "
+                        "this much wall time has passed (an idle MI355X needs about 40 ms of load "
+                        "to reach its sustained clocks; 5 steps of the 480P workload take ~95 ms, "
+                        "5 steps of the image workload only ~2.5 ms). Off by default: exactly "
+                        "--warmup steps run")
+    p.add_argument("--workload", default="c3", choices=sorted(WORKLOAD_KEYS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle sample")
