@@ -9,6 +9,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 namespace dit {
 namespace attn {
@@ -195,57 +196,150 @@ __device__ __forceinline__ bool decode_block(const int32_t* cu_q, const int32_t*
     return true;
 }
 
+#ifdef DIT_ATTN_PERSISTENT   // the bf16 attention file only (it alone holds the device state below)
 // ---- Persistent launches: one block per resident slot (CU), looping over items.
 // The XCDs of one chip run at different clocks under this load (their blocks'
 // key loops differed by up to 10% within one launch), so a fixed 1/8 of the items
 // per XCD leaves the fast XCDs idle at the end. In a persistent launch every XCD
-// draws items from its own queue -- its xcd_slice range, in order, so that its
-// concurrent blocks still share a head's K/V in its L2 -- and, once that is
-// empty, from the other XCDs' queues. A queue is an item counter in device memory
+// draws work units from its own queue -- its xcd_slice range, in order, so that
+// its concurrent blocks still share a head's K/V in its L2 -- and, once that is
+// empty, from the other XCDs' queues. A queue is a unit counter in device memory
 // (device-scope atomics); the last block to finish clears the counters for the
-// next launch that uses the same slot. Launches rotate over kQueueSlots slots, so
-// concurrently running launches (other streams) use different counters as long
-// as fewer than kQueueSlots of one kernel file are in flight on one device. The
-// counters are per translation unit (anonymous namespace): each attention kernel
-// file has its own.
+// next launch that uses the same slot.
+//
+// Tail splitting: the last T items of each XCD's range (the items of its last,
+// partly filled round; a whole round when the range divides evenly) are split
+// along the keys into s pieces each (split_plan), so the launch's last round
+// runs pieces of 1/s of an item rather than whole items. A piece writes its
+// partial result (unnormalised float32 o, running max m and row sum l per query)
+// to a scratch slot; the last piece of an item to finish (a counter per split
+// item) merges the s partials with the log-sum-exp rule and writes the item's
+// output. Pieces are only taken from their own XCD's queue (other XCDs steal
+// full items only), so a split item's pieces, their partials and the merge
+// share one L2: a piece publishes its partial by waiting for its stores before
+// its counter increment, with no L2 write-back or invalidation.
+//
+// Device state (file-scope device arrays, resolved per device with
+// hipGetSymbolAddress; nothing is allocated at call time): kQueueSlots queue
+// slots and one split scratch area. The host hands a slot to a launch only when
+// the slot's previous launch was on the same stream (stream order) or has
+// completed (an event recorded after it), and likewise the split scratch; a
+// launch that finds no free slot, or runs under stream capture, takes the
+// one-block-per-item form, which keeps no device state. The counters are per
+// translation unit (anonymous namespace): each attention kernel file has its own.
 constexpr int kQueueSlots = 64;
-constexpr int kQWords = 16;   // one 64-byte line per counter
+constexpr int kQWords = 16;      // one 64-byte line per counter
+constexpr int kSplitC = 32;      // blocks per XCD the split plan is sized for (256 CUs)
+constexpr int kSplitMaxS = 16;   // at most this many pieces per split item
+constexpr int kSplitPieces = 8 * 2 * kSplitC;   // partial slots: T s <= 2 C per XCD
+constexpr int kSplitQ = 256;     // queries per work item (the split path's block)
+constexpr int kSplitD = 128;     // head dim of the split path
+struct SplitPartial {            // one piece's partial result for its 256 queries
+    float o[kSplitQ][kSplitD];   // sum_k 2^(s_k c - m) v_k (unnormalised)
+    float m[kSplitQ];            // running max (scaled log2 domain)
+    float l[kSplitQ];            // sum_k 2^(s_k c - m)
+};
 
 namespace {
 
 __device__ uint32_t g_attn_queue[kQueueSlots][9 * kQWords];   // 8 XCD queues, then the finished-block count
+__device__ __attribute__((aligned(256))) SplitPartial g_attn_split[kSplitPieces];
+__device__ uint32_t g_attn_split_cnt[8 * kSplitC * kQWords];   // one counter (line) per split item
 
-// Per device: compute units, the counters' device address, the next slot.
+// Per device: compute units, device addresses of the arrays, and the launch
+// tracking of the slots and the split scratch.
 struct QueueDevice {
-    std::atomic<int> cus{0};
-    std::atomic<uint32_t*> queue{nullptr};
-    std::atomic<uint32_t> next_slot{0};
+    std::mutex mu;
+    bool init = false;
+    int cus = 0;
+    uint32_t* queue = nullptr;
+    SplitPartial* split = nullptr;
+    uint32_t* split_cnt = nullptr;
+    hipEvent_t ev[kQueueSlots + 1] = {};      // [kQueueSlots]: the split scratch
+    hipStream_t last[kQueueSlots + 1] = {};
+    bool used[kQueueSlots + 1] = {};
+    uint32_t next = 0;
 };
 QueueDevice g_queue_dev[64];
 
-// Host: the current device's compute-unit count and, when want_slot, a queue
-// slot for one launch.
-inline hipError_t queue_launch_info(int& cus, uint32_t*& queue_slot, bool want_slot) {
-    int dev = 0;
+inline hipError_t queue_device(QueueDevice*& out, int& dev) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     QueueDevice& d = g_queue_dev[dev];
-    int n = d.cus.load(std::memory_order_relaxed);
-    uint32_t* q = d.queue.load(std::memory_order_relaxed);
-    if (n == 0 || q == nullptr) {
-        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (!d.init) {
+        e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
-        // the array's device address on this device (its name in host code is not it)
-        e = hipGetSymbolAddress(reinterpret_cast<void**>(&q), HIP_SYMBOL(g_attn_queue));
+        // the arrays' device addresses on this device (their names in host code are not)
+        e = hipGetSymbolAddress(reinterpret_cast<void**>(&d.queue), HIP_SYMBOL(g_attn_queue));
         if (e != hipSuccess) return e;
-        d.cus.store(n, std::memory_order_relaxed);
-        d.queue.store(q, std::memory_order_relaxed);
+        e = hipGetSymbolAddress(reinterpret_cast<void**>(&d.split), HIP_SYMBOL(g_attn_split));
+        if (e != hipSuccess) return e;
+        e = hipGetSymbolAddress(reinterpret_cast<void**>(&d.split_cnt), HIP_SYMBOL(g_attn_split_cnt));
+        if (e != hipSuccess) return e;
+        for (int i = 0; i <= kQueueSlots; ++i) {
+            e = hipEventCreateWithFlags(&d.ev[i], hipEventDisableTiming);
+            if (e != hipSuccess) return e;
+        }
+        d.init = true;
     }
-    cus = n;
-    queue_slot = want_slot
-                     ? q + (size_t)(d.next_slot.fetch_add(1, std::memory_order_relaxed) % kQueueSlots) * 9 * kQWords
-                     : nullptr;
+    out = &d;
+    return hipSuccess;
+}
+
+// Host: the current device's compute-unit count.
+inline hipError_t device_cus(int& cus) {
+    QueueDevice* d = nullptr;
+    int dev = 0;
+    hipError_t e = queue_device(d, dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> g(d->mu);
+    cus = d->cus;
+    return hipSuccess;
+}
+
+// true if resource i may be used by a launch on `stream` now
+inline bool resource_free(QueueDevice& d, int i, hipStream_t stream) {
+    if (!d.used[i] || d.last[i] == stream) return true;
+    return hipEventQuery(d.ev[i]) == hipSuccess;
+}
+
+// Host: run `launch(queue_slot, split, split_cnt)` for a persistent launch on
+// `stream` with a free queue slot (and the split scratch if it is free, else
+// null), recording the slot's event after it; or, under stream capture or when
+// no slot is free, run `fallback()`. Serialised per device.
+template <class Persistent, class Fallback>
+inline hipError_t persistent_launch(hipStream_t stream, Persistent&& launch, Fallback&& fallback) {
+    QueueDevice* dp = nullptr;
+    int dev = 0;
+    hipError_t e = queue_device(dp, dev);
+    if (e != hipSuccess) return e;
+    QueueDevice& d = *dp;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return e;
+    if (cap != hipStreamCaptureStatusNone) return fallback();   // replays would share device counters
+    std::lock_guard<std::mutex> g(d.mu);
+    int slot = -1;
+    for (int t = 0; t < kQueueSlots; ++t) {
+        const int i = (int)((d.next + t) % kQueueSlots);
+        if (resource_free(d, i, stream)) { slot = i; break; }
+    }
+    if (slot < 0) return fallback();   // kQueueSlots launches in flight on other streams
+    d.next = (uint32_t)(slot + 1);
+    const bool split = resource_free(d, kQueueSlots, stream);
+    e = launch(d.queue + (size_t)slot * 9 * kQWords, split ? d.split : nullptr, split ? d.split_cnt : nullptr);
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(d.ev[slot], stream);
+    if (e != hipSuccess) return e;
+    d.used[slot] = true;
+    d.last[slot] = stream;
+    if (split) {
+        e = hipEventRecord(d.ev[kQueueSlots], stream);
+        if (e != hipSuccess) return e;
+        d.used[kQueueSlots] = true;
+        d.last[kQueueSlots] = stream;
+    }
     return hipSuccess;
 }
 
@@ -256,28 +350,100 @@ __device__ __forceinline__ int xcc_id() {
     return (int)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (31 << 11)) & 7);
 }
 
-// The next item for a block on XCD x: its own queue first, then the others in
-// turn; -1 when every queue is empty. Counters may run past their range
-// (harmless: they are cleared at the end of the launch).
-__device__ __forceinline__ int next_item(uint32_t* q, int total, int x) {
-    for (int t = 0; t < 8; ++t) {
-        const int v = (x + t) & 7;
-        int start, len;
-        xcd_slice(total, v, start, len);
-        if (len == 0) continue;
-        const uint32_t i = atomicAdd(&q[v * kQWords], 1u);
-        if (i < (uint32_t)len) return start + (int)i;
+// Split plan of one XCD's range of len items for C blocks per XCD: the last T
+// items are cut into s pieces (s = 1: no split). T = the items of the last,
+// partly filled round; s in [2, 16] with T s <= 2C minimises the last round's
+// length ceil(T s / C) / s (ties: fewer pieces). A range that divides evenly
+// has its whole last round cut in halves: the XCDs' clock differences then
+// even out, by stealing, at half-item granularity. Ranges shorter than 2
+// rounds are left whole.
+__device__ __forceinline__ void split_plan(int len, int C, bool enabled, int& T, int& s) {
+    T = 0;
+    s = 1;
+    if (!enabled || C > kSplitC || C <= 0 || len < 2 * C) return;
+    if (len % C == 0) {
+        T = C;
+        s = 2;
+        return;
     }
-    return -1;
+    const int t = len % C;
+    int best_s = 1, best_num = 1, best_den = 1;   // tail length best_num / best_den (s = 1: 1 round)
+    for (int c = 2; c <= kSplitMaxS && t * c <= 2 * C; ++c) {
+        const int num = (t * c + C - 1) / C;   // rounds of pieces
+        if (num * best_den < best_num * c) { best_s = c; best_num = num; best_den = c; }
+    }
+    if (best_s > 1) { T = t; s = best_s; }
 }
 
-// Called once per block (one thread) after its last item: the last block of the
+// Units of XCD x's queue: its full items, then T s pieces (piece-major).
+__device__ __forceinline__ int xcd_units(int len, int T, int s) { return len - T + T * s; }
+
+// The next unit for a block on XCD x: its own queue first, then the others in
+// turn. Returns the owning XCD v and the unit index u in its range, or v = -1
+// when every queue is empty. Counters may run past their range (harmless: they
+// are cleared at the end of the launch).
+__device__ __forceinline__ void next_unit(uint32_t* q, int total, int C, bool split, int x, int& v, int& u) {
+    for (int t = 0; t < 8; ++t) {
+        const int y = (x + t) & 7;
+        int start, len, T, s;
+        xcd_slice(total, y, start, len);
+        if (len == 0) continue;
+        split_plan(len, C, split, T, s);
+        if (t == 0) {   // own queue: full items, then the pieces
+            const uint32_t i = atomicAdd(&q[y * kQWords], 1u);
+            if (i < (uint32_t)xcd_units(len, T, s)) { v = y; u = (int)i; return; }
+            continue;
+        }
+        // another XCD's queue: full items only (compare-and-swap below its pieces).
+        // A split item's pieces and their merge thus share one L2, so publishing
+        // a partial needs no L2 write-back.
+        const uint32_t avail = (uint32_t)(len - T);
+        uint32_t c = __hip_atomic_load(&q[y * kQWords], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        while (c < avail) {
+            const uint32_t old = atomicCAS(&q[y * kQWords], c, c + 1);
+            if (old == c) { v = y; u = (int)c; return; }
+            c = old;
+        }
+    }
+    v = -1;
+    u = -1;
+}
+
+// Unit u of XCD v -> item index, piece (p of s; s = 1: whole item), and for a
+// piece its partial slot and counter index.
+struct Unit {
+    int item, piece, pieces, slot, counter;
+};
+__device__ __forceinline__ Unit decode_unit(int total, int C, bool split, int v, int u) {
+    int start, len, T, s;
+    xcd_slice(total, v, start, len);
+    split_plan(len, C, split, T, s);
+    Unit r;
+    if (u < len - T) {
+        r.item = start + u;
+        r.piece = 0;
+        r.pieces = 1;
+        r.slot = r.counter = -1;
+    } else {
+        const int i = u - (len - T);
+        const int it = i % T;
+        r.piece = i / T;
+        r.pieces = s;
+        r.item = start + len - T + it;
+        r.slot = v * 2 * kSplitC + it * s + r.piece;
+        r.counter = (v * kSplitC + it) * kQWords;
+    }
+    return r;
+}
+
+// Called once per block (one thread) after its last unit: the last block of the
 // launch clears the slot's counters.
 __device__ __forceinline__ void queue_finish(uint32_t* q, int nblocks) {
     __threadfence();
     if (atomicAdd(&q[8 * kQWords], 1u) == (uint32_t)(nblocks - 1))
         for (int i = 0; i < 9; ++i) __hip_atomic_store(&q[i * kQWords], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+#endif  // DIT_ATTN_PERSISTENT
 
 }  // namespace attn
 }  // namespace dit

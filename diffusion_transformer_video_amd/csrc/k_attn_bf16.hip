@@ -51,6 +51,7 @@
 //     at different clocks under this load; see dit_attn_common.hpp).
 #include <math.h>
 
+#define DIT_ATTN_PERSISTENT
 #include "dit_attn_common.hpp"
 #include "dit_device.hpp"
 #include "dit_internal.h"
@@ -66,6 +67,18 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLazyRescale = 8.0f;   // log2 headroom before the max is raised
+// The persistent launch (per-XCD queues, split tail) is used from 4 work items
+// per resident block (the queues even out the XCDs' clock differences), and from
+// 2 when a one-block-per-item launch would leave its last round less than 90%
+// full (the split tail fills it). Measured: 480P +0% / 720P +2% / one GPU's
+// Ulysses share (2.5 items per block) +10% against one block per item; the image
+// workload (3 whole rounds) is 6% faster with one block per item.
+__host__ __forceinline__ bool use_persistent(int64_t grid, int64_t resident) {
+    if (resident < 8) return false;
+    if (grid >= 4 * resident) return true;
+    const int64_t last = grid % resident;
+    return grid >= 2 * resident && last != 0 && 10 * last < 9 * resident;
+}
 
 template <int HD, int NW>
 struct Cfg {
@@ -466,7 +479,8 @@ __device__ __forceinline__ void pipe_last(Pipe<HD, NW, QB>& p, const f32x16 (&S)
 template <int HD, int NW, int QB>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, const attn::BlockWork& bw,
                                           char (&kbuf)[Cfg<HD, NW>::ST][Cfg<HD, NW>::TILEB],
-                                          char (&vbuf)[Cfg<HD, NW>::ST][Cfg<HD, NW>::TILEB], int tid) {
+                                          char (&vbuf)[Cfg<HD, NW>::ST][Cfg<HD, NW>::TILEB], int tid,
+                                          attn::SplitPartial* part = nullptr) {
     using C = Cfg<HD, NW>;
     constexpr int BQ = 32 * QB * NW;   // queries per block
     const int head = bw.head, qt = bw.qt, len = bw.len, klen = bw.klen;
@@ -592,6 +606,27 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const attn::BlockWo
     if (p.ntiles > 1) pipe_step_rt<HD, NW, QB, true>(p, p.ntiles - 2, S);
     pipe_last<HD, NW, QB>(p, S, (uint32_t)((p.ntiles - 1) % C::ST) * C::TILEB);
 
+    if (part != nullptr) {   // a piece of a split item: the unnormalised partial, m and l
+        if constexpr (HD == attn::kSplitD && 32 * QB * NW == attn::kSplitQ) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const int ql = 32 * (QB * p.wave + qb) + l32;   // query within the item
+#pragma unroll
+                for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg)
+                        *reinterpret_cast<float4*>(&part->o[ql][dt * 32 + 8 * rg + 4 * p.g]) =
+                            make_float4(p.O[qb][dt][4 * rg], p.O[qb][dt][4 * rg + 1], p.O[qb][dt][4 * rg + 2],
+                                        p.O[qb][dt][4 * rg + 3]);
+                const float l = pair_sum(p.l_run[qb]);
+                if (p.g == 0) {
+                    part->m[ql] = p.m_run[qb];
+                    part->l[ql] = l;
+                }
+            }
+        }
+        return;
+    }
     // ---- normalise and store: lane holds query my_q[qb], d = 32dt + 8(r/4) + 4g + r%4;
     // lanes l and l^32 summed disjoint keys of the same query.
     // The sequence's rows of o (and lse) for this head, as range-checked buffers:
@@ -639,12 +674,128 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     attn_item<HD, NW, QB>(a, bw, kbuf, vbuf, thread_index());
 }
 
-// ---- Persistent launch (work queues: dit_attn_common.hpp)
+// ---- Persistent launch (work queues and tail splitting: dit_attn_common.hpp)
 struct AttnLaunch {
     AttnArgs a;
     int nqt, nblocks;
-    uint32_t* queue;   // this launch's slot of g_attn_queue
+    uint32_t* queue;              // this launch's queue slot
+    attn::SplitPartial* split;    // partial slots, or null: no tail splitting
+    uint32_t* split_cnt;          // completion counters of the split items
 };
+
+// Merge of the s partials of one split item (slots slot0 .. slot0 + s - 1) into
+// its output rows: per query, M = max m_p, L = sum l_p 2^(m_p - M),
+// o = sum 2^(m_p - M) o_p / L, lse = ln 2 (M + log2 L); no keys at all (M = -inf)
+// gives o = 0, lse = -inf. Two threads per query, 64 dims each.
+template <int NW>
+__device__ __forceinline__ void merge_pieces(const AttnArgs& a, const attn::BlockWork& bw,
+                                             const attn::SplitPartial* parts, int s, int tid) {
+    constexpr int D = attn::kSplitD;
+    for (int t = tid; t < 2 * attn::kSplitQ; t += 64 * NW) {
+        const int ql = t >> 1, h = t & 1;
+        const int qi = bw.qt * attn::kSplitQ + ql;
+        if (qi >= bw.len) continue;
+        float M = -INFINITY;
+        for (int pc = 0; pc < s; ++pc) M = __builtin_fmaxf(M, parts[pc].m[ql]);
+        const int64_t row = (bw.s0 + qi) * a.heads + bw.head;
+        uint4* Og = reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(a.o) + row * D) + h * (D / 16);
+        if (M == -INFINITY) {
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) Og[c] = make_uint4(0, 0, 0, 0);
+            if (a.lse != nullptr && h == 0) a.lse[row] = -INFINITY;
+            continue;
+        }
+        float acc[D / 2];
+#pragma unroll
+        for (int i = 0; i < D / 2; ++i) acc[i] = 0.f;
+        float L = 0.f;
+        for (int pc = 0; pc < s; ++pc) {
+            const float w = __builtin_amdgcn_exp2f(parts[pc].m[ql] - M);
+            L = fmaf(w, parts[pc].l[ql], L);
+            const float4* src = reinterpret_cast<const float4*>(&parts[pc].o[ql][h * (D / 2)]);
+#pragma unroll
+            for (int i = 0; i < D / 8; ++i) {
+                const float4 v = src[i];
+                acc[4 * i] = fmaf(w, v.x, acc[4 * i]);
+                acc[4 * i + 1] = fmaf(w, v.y, acc[4 * i + 1]);
+                acc[4 * i + 2] = fmaf(w, v.z, acc[4 * i + 2]);
+                acc[4 * i + 3] = fmaf(w, v.w, acc[4 * i + 3]);
+            }
+        }
+        const float inv = 1.0f / L;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+            Og[c] = make_uint4(pack_bf16x2(acc[8 * c] * inv, acc[8 * c + 1] * inv),
+                               pack_bf16x2(acc[8 * c + 2] * inv, acc[8 * c + 3] * inv),
+                               pack_bf16x2(acc[8 * c + 4] * inv, acc[8 * c + 5] * inv),
+                               pack_bf16x2(acc[8 * c + 6] * inv, acc[8 * c + 7] * inv));
+        if (a.lse != nullptr && h == 0) a.lse[row] = (M + __log2f(L)) * 0.69314718055994531f;
+    }
+}
+
+// Piece p of s of a split item covers key tiles p nt / s .. (p + 1) nt / s - 1
+// (possibly none): narrow the item to those keys. Returns false for an empty
+// piece, whose partial (m = -inf, l = 0) is written here.
+template <int NW, int BK>
+__device__ __forceinline__ bool piece_keys(attn::BlockWork& bw, const attn::Unit& un, attn::SplitPartial* part,
+                                           int tid) {
+    const int nt = (bw.klen + BK - 1) / BK;
+    const int t0 = un.piece * nt / un.pieces, t1 = (un.piece + 1) * nt / un.pieces;
+    const int k_lo = t0 * BK, k_hi = t1 * BK < bw.klen ? t1 * BK : bw.klen;
+    if (k_hi > k_lo) {
+        bw.k0 += k_lo;
+        bw.klen = k_hi - k_lo;
+        return true;
+    }
+    for (int q = tid; q < attn::kSplitQ; q += 64 * NW) {
+        part->m[q] = -INFINITY;
+        part->l[q] = 0.f;
+    }
+    return false;
+}
+
+// After a piece's partial is stored: if it is the item's last piece to finish,
+// merge. The pieces of an item all run on one XCD (one L2): each wave waits for
+// its partial stores to be acknowledged (by the L2) before the barrier, thread
+// 0 then increments the item's counter; the last piece reads the partials after
+// seeing the count (its L1 holds none of them: each slot is read once per
+// launch, and the L1 is invalidated at every kernel start). The last piece
+// clears the counter.
+template <int NW>
+__device__ __forceinline__ void piece_done(const AttnArgs& a, const attn::BlockWork& bw, const attn::Unit& un,
+                                           attn::SplitPartial* split, uint32_t* split_cnt, int tid, int& s_flag) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // every wave's partial stores have completed
+    if (tid == 0) {
+        const uint32_t done = atomicAdd(&split_cnt[un.counter], 1u);
+        s_flag = done == (uint32_t)(un.pieces - 1);
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(s_flag)) {
+        merge_pieces<NW>(a, bw, split + (un.slot - un.piece), un.pieces, tid);
+        if (tid == 0) __hip_atomic_store(&split_cnt[un.counter], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// The kernel's argument block, as a constant-memory pointer redefined at each
+// use (see the persistent loop), and the attention arguments read from it.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* kernargs() {
+    uint64_t p = reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
+    asm volatile("" : "+s"(p));
+    p = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p >> 32)) << 32) |
+        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    return (const __attribute__((address_space(4))) T*)p;
+}
+__device__ __forceinline__ AttnArgs load_args(const __attribute__((address_space(4))) AttnLaunch* lp) {
+    AttnArgs a;
+    a.o = lp->a.o; a.q = lp->a.q; a.k = lp->a.k; a.v = lp->a.v;
+    a.tokens = lp->a.tokens; a.heads = lp->a.heads; a.head_dim = lp->a.head_dim;
+    a.cu_seqlens = lp->a.cu_seqlens; a.num_seqs = lp->a.num_seqs; a.max_seqlen = lp->a.max_seqlen;
+    a.scale_log2 = lp->a.scale_log2; a.scale = lp->a.scale;
+    a.cu_seqlens_k = lp->a.cu_seqlens_k; a.max_seqlen_k = lp->a.max_seqlen_k; a.lse = lp->a.lse;
+    return a;
+}
 
 template <int HD, int NW, int QB>
 __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf16_persistent(AttnLaunch L) {
@@ -652,41 +803,66 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     constexpr int BQ = 32 * QB * NW;
     __shared__ __attribute__((aligned(1024))) char kbuf[C::ST][C::TILEB];
     __shared__ __attribute__((aligned(1024))) char vbuf[C::ST][C::TILEB];
-    __shared__ int s_item;
+    __shared__ int s_item, s_unit, s_flag;
     typedef __attribute__((address_space(4))) const AttnLaunch* kernarg_ptr;   // constant memory: scalar loads
 
     const int total = attn::items_total(L.a.cu_seqlens, L.a.num_seqs, L.a.heads, L.nqt, BQ);
-    const int xcc = attn::xcc_id();
     for (;;) {
         // The launch arguments, the item count and the thread index are redefined
         // here for every item (empty asm, no instruction; the pointer is read back
         // through readfirstlane, since asm outputs count as divergent): otherwise
         // they and everything derived from them are computed once and held in
         // registers through every key loop, where the scalar registers are already
-        // all in use.
-        uint64_t lpv = reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
+        // all in use. For the same reason nothing about the unit is kept across
+        // the item: a split piece's completion re-derives it from the LDS copy.
+        const kernarg_ptr lp = kernargs<AttnLaunch>();
         int tt = total, tid = thread_index();
-        asm volatile("" : "+s"(lpv), "+s"(tt), "+v"(tid));
-        lpv = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(lpv >> 32)) << 32) |
-              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)lpv);
+        asm volatile("" : "+s"(tt), "+v"(tid));
         tt = __builtin_amdgcn_readfirstlane(tt);
-        const kernarg_ptr lp = (kernarg_ptr)lpv;
-        AttnArgs a;
-        a.o = lp->a.o; a.q = lp->a.q; a.k = lp->a.k; a.v = lp->a.v;
-        a.tokens = lp->a.tokens; a.heads = lp->a.heads; a.head_dim = lp->a.head_dim;
-        a.cu_seqlens = lp->a.cu_seqlens; a.num_seqs = lp->a.num_seqs; a.max_seqlen = lp->a.max_seqlen;
-        a.scale_log2 = lp->a.scale_log2; a.scale = lp->a.scale;
-        a.cu_seqlens_k = lp->a.cu_seqlens_k; a.max_seqlen_k = lp->a.max_seqlen_k; a.lse = lp->a.lse;
+        // blocks per XCD (the dispatcher deals blocks round-robin), and whether this
+        // launch splits its tail (partial slots given, 256 queries x 128 dims per item)
+        const int bpx = lp->nblocks / 8;
+        const bool split =
+            lp->split != nullptr && lp->nblocks % 8 == 0 && HD == attn::kSplitD && BQ == attn::kSplitQ;
+        AttnArgs a = load_args(lp);
 
         __syncthreads();   // the previous item's LDS reads, and every wave's read of s_item, are done
-        if (tid == 0) s_item = attn::next_item(lp->queue, tt, xcc);
+        if (tid == 0) {
+            int v, u;
+            attn::next_unit(lp->queue, tt, bpx, split, attn::xcc_id(), v, u);
+            s_item = v;
+            s_unit = u;
+        }
         __syncthreads();
-        const int w = __builtin_amdgcn_readfirstlane(s_item);
-        if (w < 0) break;
-        attn::BlockWork bw;
-        attn::decode_item(w, a.cu_seqlens, a.cu_seqlens_k, a.num_seqs, a.max_seqlen, a.max_seqlen_k, lp->nqt, BQ, tt,
-                          a.heads, bw);
-        attn_item<HD, NW, QB>(a, bw, kbuf, vbuf, tid);
+        const int v = __builtin_amdgcn_readfirstlane(s_item);
+        if (v < 0) break;
+        {
+            const attn::Unit un = attn::decode_unit(tt, bpx, split, v, __builtin_amdgcn_readfirstlane(s_unit));
+            attn::BlockWork bw;
+            attn::decode_item(un.item, a.cu_seqlens, a.cu_seqlens_k, a.num_seqs, a.max_seqlen, a.max_seqlen_k,
+                              lp->nqt, BQ, tt, a.heads, bw);
+            // a piece of a split item: its keys only, its partial into its slot
+            attn::SplitPartial* part = un.pieces > 1 ? lp->split + un.slot : nullptr;
+            const bool keys = part == nullptr || piece_keys<NW, Cfg<HD, NW>::BK>(bw, un, part, tid);
+            if (keys) attn_item<HD, NW, QB>(a, bw, kbuf, vbuf, tid, part);
+        }
+        {
+            const kernarg_ptr lq = kernargs<AttnLaunch>();
+            int t2 = total, tid2 = thread_index();
+            asm volatile("" : "+s"(t2), "+v"(tid2));
+            t2 = __builtin_amdgcn_readfirstlane(t2);
+            const bool split2 =
+                lq->split != nullptr && lq->nblocks % 8 == 0 && HD == attn::kSplitD && BQ == attn::kSplitQ;
+            const attn::Unit un = attn::decode_unit(t2, lq->nblocks / 8, split2, __builtin_amdgcn_readfirstlane(s_item),
+                                                    __builtin_amdgcn_readfirstlane(s_unit));
+            if (un.pieces > 1) {
+                const AttnArgs a2 = load_args(lq);
+                attn::BlockWork whole;
+                attn::decode_item(un.item, a2.cu_seqlens, a2.cu_seqlens_k, a2.num_seqs, a2.max_seqlen,
+                                  a2.max_seqlen_k, lq->nqt, BQ, t2, a2.heads, whole);
+                piece_done<NW>(a2, whole, un, lq->split, lq->split_cnt, tid2, s_flag);
+            }
+        }
     }
     // the last block to finish clears this slot's counters for its next launch
     if (thread_index() == 0) {
@@ -702,20 +878,27 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     int cus = 0;
-    uint32_t* queue = nullptr;
-    hipError_t e = attn::queue_launch_info(cus, queue, false);
+    hipError_t e = attn::device_cus(cus);
     if (e != hipSuccess) return e;
     const int64_t resident = (int64_t)cus * ((QB == 1 && NW == 4) ? 2 : 1);   // blocks the chip holds at once
-    if (grid >= 4 * resident && resident >= 8) {
-        // enough items per resident block for the queues to even out the XCDs
-        e = attn::queue_launch_info(cus, queue, true);
-        if (e != hipSuccess) return e;
-        const AttnLaunch L{a, nqt, (int)resident, queue};
-        hipLaunchKernelGGL((attn_bf16_persistent<HD, NW, QB>), dim3((unsigned)resident), dim3(64 * NW), 0, s, L);
-    } else {
+    auto per_item = [&]() -> hipError_t {
         hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, QB>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a, nqt);
+        return hipGetLastError();
+    };
+    if (use_persistent(grid, resident)) {
+        // enough items per resident block for the queues (and the split tail) to
+        // even out the XCDs
+        return attn::persistent_launch(
+            s,
+            [&](uint32_t* queue, attn::SplitPartial* split, uint32_t* split_cnt) -> hipError_t {
+                const AttnLaunch L{a, nqt, (int)resident, queue, split, split_cnt};
+                hipLaunchKernelGGL((attn_bf16_persistent<HD, NW, QB>), dim3((unsigned)resident), dim3(64 * NW), 0,
+                                   s, L);
+                return hipGetLastError();
+            },
+            per_item);
     }
-    return hipGetLastError();
+    return per_item();
 }
 
 }  // namespace

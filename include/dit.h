@@ -37,9 +37,10 @@
  *
  * Conventions shared by every entry point:
  *   - Pointers to tensors are DEVICE pointers owned by the caller. The library
- *     allocates no device memory at call time. Its only device state is a fixed
- *     array of work-queue counters, loaded with the library, that large bf16
- *     attention launches use and leave cleared (see dit_attn3d).
+ *     allocates no device memory at call time. Its only device state is loaded
+ *     with the library, per device: 64 slots of work-queue counters and one
+ *     array of split-item partials (512 x 130 KiB = 65 MiB, with its counters)
+ *     that large bf16 attention launches use and leave cleared (see dit_attn3d).
  *   - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue work
  *     on it and never synchronise; results are visible after the stream is
  *     synchronised. Faults inside a running kernel surface at that sync.
@@ -132,11 +133,25 @@ int dit_rope3d(void* q, void* k, int64_t tokens, int32_t heads, int32_t head_dim
  *   head_dim in {64, 128} (else DIT_E_UNSUPPORTED)
  * bf16 runs on MFMA with float32 accumulation; probabilities enter the second
  * product rounded to bf16. float32 runs on the vector ALUs in full float32.
- * Large bf16 launches (at least 4 query tiles of 256 (128 at head_dim 64) per
- * block the device holds at once) run one block per compute unit drawing work
- * from counters in library-owned device memory: at most 64 such launches
- * (dit_attn3d and dit_attn3d_lse together) may be in flight on one device at
- * once, e.g. on different streams. Results do not depend on the launch form.
+ * Launch forms. Let G be the number of query tiles (256 queries, 128 at
+ * head_dim 64) times heads times sequences, and R the blocks the device holds at
+ * once (one per compute unit; two at head_dim 64). With G >= 4R, or G >= 2R and a
+ * last round of one-block-per-tile under 90% full, R persistent blocks draw
+ * tiles from per-XCD queues (counters in library-owned device memory; a block
+ * takes tiles of its own XCD first, then steals). At head_dim 128 the tiles of
+ * each queue's last round are also cut along their keys into 2..16 pieces whose
+ * partial results (unnormalised o, running max, row sum) go to the library's
+ * split array; the last piece of a tile to finish merges them. Otherwise, and
+ * always under stream capture, one block per tile.
+ * Concurrency: each persistent launch takes one of 64 counter slots and, if no
+ * unfinished launch on another stream holds it, the split array. Slots and the
+ * split array are tracked with events, so concurrent launches on several streams
+ * are safe; with all 64 slots held by unfinished launches on other streams a
+ * launch runs one block per tile, and without the split array it runs unsplit.
+ * Results: unsplit tiles are bitwise identical in every form; a split tile sums
+ * its key blocks in another order (same float32 arithmetic, agreement within
+ * rounding). For a given shape and device, repeated launches give identical bits
+ * unless a concurrent launch on another stream holds the split array.
  */
 int dit_attn3d(void* o, const void* q, const void* k, const void* v,
                int64_t tokens, int32_t heads, int32_t head_dim,
@@ -165,7 +180,8 @@ int dit_attn3d(void* o, const void* q, const void* k, const void* v,
  *                must be >= every query / key count (unchecked precondition);
  *                key counts may be 0
  *   head_dim in {64, 128} (else DIT_E_UNSUPPORTED); tokens_q, tokens_k >= 1
- * Arithmetic as dit_attn3d, which is the case k, v = the queries' own tokens.
+ * Arithmetic and launch forms as dit_attn3d, which is the case k, v = the
+ * queries' own tokens.
  */
 int dit_attn3d_lse(void* o, float* lse, const void* q, const void* k, const void* v,
                    int64_t tokens_q, int64_t tokens_k, int32_t heads, int32_t head_dim,

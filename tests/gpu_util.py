@@ -57,3 +57,65 @@ def sample_rows(w, per_seq=48, edge=8, seed=99):
 
 def note(msg):
     print(msg, flush=True)
+
+
+# ---- the persistent attention launch's tail split, replicated from its
+# definition (dit_attn_common.hpp): which work items a launch cuts into pieces
+def xcd_slice(total, x):
+    per, rem = divmod(total, 8)
+    ln = per + (1 if x < rem else 0)
+    start = x * (per + 1) if x < rem else rem * (per + 1) + (x - rem) * per
+    return start, ln
+
+
+def split_plan(ln, C, max_s=16):
+    """(T, s): the last T items of an XCD range of ln items are cut into s pieces."""
+    if C > 32 or C <= 0 or ln < 2 * C:
+        return 0, 1
+    if ln % C == 0:
+        return C, 2
+    t = ln % C
+    best, bn, bd = 1, 1, 1
+    for c in range(2, max_s + 1):
+        if t * c > 2 * C:
+            break
+        num = -(-(t * c) // C)
+        if num * bd < bn * c:
+            best, bn, bd = c, num, c
+    return (t, best) if best > 1 else (0, 1)
+
+
+def split_items(total, cus):
+    """{item index: pieces} of a persistent launch of `total` work items on a
+    device with `cus` compute units (one block per unit)."""
+    out = {}
+    if cus % 8:
+        return out
+    C = cus // 8
+    for x in range(8):
+        start, ln = xcd_slice(total, x)
+        T, s = split_plan(ln, C)
+        for i in range(start + ln - T, start + ln):
+            out[i] = s
+    return out
+
+
+def item_rows(w, item, bq=256):
+    """Work item -> (head, token rows) for the attention work numbering: head-major
+    over the query tiles of every sequence, longest sequence first (index order
+    among equals, or plain index order past 32 sequences)."""
+    lens = [int(w.cu_seqlens[s + 1] - w.cu_seqlens[s]) for s in range(w.num_seqs)]
+    tiles = [-(-n // bq) for n in lens]
+    per_head = sum(tiles)
+    head, r = divmod(item, per_head)
+    order = list(range(w.num_seqs)) if w.num_seqs > 32 else sorted(range(w.num_seqs), key=lambda s: (-lens[s], s))
+    for s in order:
+        if r < tiles[s]:
+            lo = int(w.cu_seqlens[s]) + r * bq
+            return head, np.arange(lo, min(lo + bq, int(w.cu_seqlens[s + 1])), dtype=np.int64)
+        r -= tiles[s]
+    raise ValueError(item)
+
+
+def attn_items_total(w, bq=256):
+    return w.heads * sum(-(-int(w.cu_seqlens[s + 1] - w.cu_seqlens[s]) // bq) for s in range(w.num_seqs))

@@ -7,7 +7,7 @@ import torch
 
 import diffusion_transformer_video_amd as dit
 import synth
-from gpu_util import TOL, dev, host64, maxabs, need_gpu, note, sample_rows
+from gpu_util import TOL, attn_items_total, dev, host64, item_rows, maxabs, need_gpu, note, sample_rows, split_items
 from oracle import attention as o_attn
 
 pytestmark = pytest.mark.gpu
@@ -85,9 +85,44 @@ def test_c1_tiny_block_f32():
     _check(synth.C1)
 
 
-@pytest.mark.parametrize("w", [synth.C2, synth.C3, synth.C4, synth.C5], ids=lambda w: w.name)
-def test_full_size_sampled_rows(w):
-    _check(w, rows=sample_rows(w, per_seq=48 if w.tokens > 10000 else 128))
+def tile_rows(w, n_random=2048, bq=256, seed=7):
+    """Rows that reach every work item of every head at full size: the first and
+    last rows of every sequence, one seeded row inside every 256-query tile of
+    every sequence, and n_random seeded rows over all tokens."""
+    r = np.random.default_rng(seed)
+    rows = list(sample_rows(w, per_seq=0, edge=4))
+    for s in range(w.num_seqs):
+        lo, hi = int(w.cu_seqlens[s]), int(w.cu_seqlens[s + 1])
+        for t0 in range(lo, hi, bq):
+            rows.append(int(r.integers(t0, min(t0 + bq, hi))))
+    rows += list(r.choice(w.tokens, size=min(n_random, w.tokens), replace=False))
+    return np.unique(np.asarray(rows, dtype=np.int64))
+
+
+def test_full_size_image_every_row():
+    """The image workload (2 x 4,096 tokens, 24 heads): every output row."""
+    _check(synth.C2)
+
+
+@pytest.mark.parametrize("w", [synth.C3, synth.C4, synth.C5], ids=lambda w: w.name)
+def test_full_size_tile_rows(w):
+    """Video and packed workloads: a row in every 256-query tile of every
+    sequence (so every work item of every head is compared), sequence edges,
+    and 2,048 seeded rows, all heads, exact full-row softmax."""
+    _check(w, rows=tile_rows(w))
+
+
+@pytest.mark.parametrize("w", [synth.C3, synth.C4, synth.C5], ids=lambda w: w.name)
+def test_full_size_one_whole_head(w):
+    """Every row of one seeded head at full size."""
+    need_gpu()
+    h = int(np.random.default_rng(w.seed).integers(w.heads))
+    inp = synth.make(w, ["q", "k", "v"])
+    got = _run(w, inp)[:, h]
+    ref = o_attn.attention(inp["q"][:, h:h + 1], inp["k"][:, h:h + 1], inp["v"][:, h:h + 1], w.cu_seqlens)[:, 0]
+    err = maxabs(got, ref)
+    note(f"attn {w.name} head {h}, every row: max-abs {err:.3e}")
+    assert err <= TOL[w.dtype]
 
 
 # Launches with at least 4 work items per resident block take the persistent
@@ -106,14 +141,23 @@ def test_persistent_launch_sampled_rows(hd, heads):
 @pytest.mark.parametrize("hd,heads", PERSISTENT, ids=[f"hd{hd}" for hd, _ in PERSISTENT])
 def test_persistent_equals_per_item_launch(hd, heads):
     """The 300-token sequence of the persistent launch above, bit for bit the
-    same as that sequence attended alone (a one-block-per-item launch)."""
+    same as that sequence attended alone (a one-block-per-item launch), on
+    every head whose items the persistent launch did not split along the keys
+    (split items sum their keys in pieces: checked against the oracle in
+    test_split_tail_against_oracle)."""
     need_gpu()
     big = _seq_workload(f"pers{hd}", "bf16", (8192, 300), heads, hd)
     inp = synth.make(big, ["q", "k", "v"])
     got_big = _run(big, inp)
     small = _seq_workload(f"pers{hd}_tail", "bf16", (300,), heads, hd)
     got_small = _run(small, {n: inp[n][8192:] for n in ("q", "k", "v")})
-    assert np.array_equal(got_big[8192:], got_small)
+    split_heads = set()
+    if hd == 128:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        split_heads = {item_rows(big, i)[0] for i in split_items(attn_items_total(big), cus)}
+    keep = [h for h in range(heads) if h not in split_heads]
+    assert keep
+    assert np.array_equal(got_big[8192:, keep], got_small[:, keep])
 
 
 def test_persistent_launch_many_sequences():
@@ -189,3 +233,58 @@ def test_rows_past_end_untouched():
     dit.dit_attn3d(o, q, k, v, cu_seqlens=torch.from_numpy(w.cu_seqlens).cuda(), max_seqlen=130)
     torch.cuda.synchronize()
     assert torch.all(buf[:32] == 7.0) and torch.all(buf[32 + w.tokens:] == 7.0)
+
+
+# The persistent launch cuts the last work items of each XCD's range along the
+# keys (pieces merged by log-sum-exp in the kernel); these shapes put different
+# plans on the tail: 480P (the whole last round in halves), 720P (one item per
+# XCD in 16 pieces), one GPU's Ulysses share (16 items per XCD in halves),
+# ragged packed sequences, and short sequences with more pieces than key tiles
+# (empty pieces).
+SPLIT_CASES = {
+    "video480p": lambda: synth.C3,
+    "video720p": lambda: synth.C4,
+    "ulysses_share": lambda: synth.Workload("c3_share_5heads", "bf16", (30, 52), (21,), (32760,), 5, 128,
+                                            (44, 42, 42), 10000.0, 32760, 1103),
+    "ragged": lambda: _seq_workload("split_ragged", "bf16", (1000, 513, 77), 80, 128, seed=23),
+    "empty_pieces": lambda: _seq_workload("split_empty", "bf16", (2000, 50), 200, 128, seed=29),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SPLIT_CASES))
+def test_split_tail_against_oracle(case):
+    """Every row of every split work item (its head) against the oracle, plus one
+    unsplit item per XCD range as a control; the launch's plan is computed from
+    the device's compute-unit count."""
+    need_gpu()
+    w = SPLIT_CASES[case]()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    total = attn_items_total(w)
+    plan = split_items(total, cus)
+    if not plan:
+        pytest.skip(f"{total} items on {cus} compute units: no split tail")
+    inp = synth.make(w, ["q", "k", "v"])
+    q, k, v = (dev(inp[n], w) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    if w.dense:
+        dit.dit_attn3d(o, q, k, v, num_seqs=w.num_seqs)
+    else:
+        dit.dit_attn3d(o, q, k, v, cu_seqlens=torch.from_numpy(w.cu_seqlens).cuda(), max_seqlen=w.max_seqlen)
+    torch.cuda.synchronize()
+    items = sorted(plan)
+    # a control: the first item of every XCD range is never split
+    items += [x * (total // 8) for x in range(8)]
+    by_head = {}
+    for it in items:
+        h, rows = item_rows(w, it)
+        by_head.setdefault(h, []).append(rows)
+    worst = 0.0
+    for h, parts in by_head.items():
+        rows = np.unique(np.concatenate(parts))
+        ref = o_attn.attention(inp["q"][:, h:h + 1], inp["k"][:, h:h + 1], inp["v"][:, h:h + 1], w.cu_seqlens,
+                               rows=rows)[:, 0]
+        got = host64(o[torch.from_numpy(rows).cuda(), h])
+        worst = max(worst, maxabs(got, ref))
+    note(f"split tail {case}: {len(plan)} split items ({sorted(set(plan.values()))} pieces), "
+         f"{len(by_head)} heads checked, max-abs {worst:.3e}")
+    assert worst <= TOL["bf16"]
