@@ -208,3 +208,33 @@ def test_deterministic():
         outs.append(o)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
+
+
+def test_quantisation_guard_and_determinism():
+    """The quantisation writes exactly its outputs (canaries around the q and k
+    codes and the amax table keep their values) and is deterministic."""
+    need_gpu()
+    (q, k, v), cu = _inputs([300, 65], heads=3, seed=9)
+    tokens, heads, hd = q.shape
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).cuda()
+    qd, kd, vd = d(q), d(k), d(v)
+    cut = torch.from_numpy(np.asarray(cu, np.int32)).cuda()
+    vs = dit.dit_fp8_v_stride(tokens, 2)
+    outs = []
+    for _ in range(2):
+        pad = 4096
+        bq8 = torch.full((tokens * heads * hd + 2 * pad,), 0x5A, dtype=torch.uint8, device="cuda")
+        bk8 = torch.full_like(bq8, 0x5A)
+        ba = torch.full((3 * heads + 2 * 64,), 7.0, dtype=torch.float32, device="cuda")
+        q8 = bq8[pad:pad + tokens * heads * hd].view(tokens, heads, hd)
+        k8 = bk8[pad:pad + tokens * heads * hd].view(tokens, heads, hd)
+        amax = ba[64:64 + 3 * heads].view(3, heads)
+        v8t = torch.zeros((heads, hd, vs), dtype=torch.uint8, device="cuda")
+        dit.dit_quant_fp8(q8, k8, v8t, amax, qd, kd, vd, cut, 2, 300)
+        torch.cuda.synchronize()
+        for b in (bq8, bk8):
+            assert bool(torch.all(b[:pad] == 0x5A)) and bool(torch.all(b[-pad:] == 0x5A))
+        assert bool(torch.all(ba[:64] == 7.0)) and bool(torch.all(ba[-64:] == 7.0))
+        outs.append((q8.clone(), k8.clone(), v8t.clone(), amax.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

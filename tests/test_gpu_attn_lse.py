@@ -236,3 +236,30 @@ def test_lse_deterministic():
     a = _attn_lse(q, k, v, _cu(lens), _cu(klens), "bf16")
     b = _attn_lse(q, k, v, _cu(lens), _cu(klens), "bf16")
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_merge_guard_and_determinism():
+    """The merge writes exactly the accumulator and its lse (canaries around
+    both keep their values) and is deterministic."""
+    need_gpu()
+    r = np.random.default_rng(31)
+    n, h, hd = 333, 2, 128
+    oa = r.standard_normal((n, h, hd)).astype(np.float32)
+    ob = synth.bf16_round(r.standard_normal((n, h, hd)).astype(np.float32))
+    la = (r.standard_normal((n, h)) * 3).astype(np.float32)
+    lb = (r.standard_normal((n, h)) * 3).astype(np.float32)
+    outs = []
+    for _ in range(2):
+        pad = 1024
+        bo = torch.full((n * h * hd + 2 * pad,), 7.0, dtype=torch.float32, device="cuda")
+        bl = torch.full((n * h + 2 * pad,), 7.0, dtype=torch.float32, device="cuda")
+        acc = bo[pad:pad + n * h * hd].view(n, h, hd)
+        lacc = bl[pad:pad + n * h].view(n, h)
+        acc.copy_(torch.from_numpy(oa))
+        lacc.copy_(torch.from_numpy(la))
+        dit.dit_attn_merge(acc, lacc, _dev(ob, "bf16"), torch.from_numpy(lb).cuda())
+        torch.cuda.synchronize()
+        for b in (bo, bl):
+            assert bool(torch.all(b[:pad] == 7.0)) and bool(torch.all(b[-pad:] == 7.0))
+        outs.append((acc.clone(), lacc.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])

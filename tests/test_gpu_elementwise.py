@@ -23,23 +23,29 @@ SMALL = [
 FULL = [synth.C2, synth.C3, synth.C4, synth.C5]
 
 
+CHUNK = 8192   # token rows per oracle chunk at full size (bounds host memory)
+
+
+def _chunks(rows):
+    for i in range(0, len(rows), CHUNK):
+        yield rows[i:i + CHUNK]
+
+
 def _modulate_case(w, rows=None):
+    """Every element (rows=None), compared chunk by chunk, or the given rows."""
     need_gpu()
     inp = synth.make(w, ["x", "gamma", "beta"])
     x = dev(inp["x"], w)
     y = torch.empty_like(x)
     dit.dit_adaln_modulate(y, x, dev(inp["gamma"]), dev(inp["beta"]), w.tokens_per_row, w.eps)
     torch.cuda.synchronize()
-    if rows is None:
-        ref = o_mod.adaln_modulate(inp["x"], inp["gamma"], inp["beta"], w.tokens_per_row, w.eps)
-        got = host64(y)
-    else:
-        rt = torch.from_numpy(rows).cuda()
-        ref = o_mod.adaln_modulate(inp["x"][rows], inp["gamma"][rows // w.tokens_per_row],
-                                   inp["beta"][rows // w.tokens_per_row], 1, w.eps)
-        got = host64(y[rt])
-    err = maxabs(got, ref)
-    note(f"modulate {w.name}: max-abs {err:.3e}")
+    rows = np.arange(w.tokens, dtype=np.int64) if rows is None else rows
+    err = 0.0
+    for c in _chunks(rows):
+        ref = o_mod.adaln_modulate(inp["x"][c], inp["gamma"][c // w.tokens_per_row],
+                                   inp["beta"][c // w.tokens_per_row], 1, w.eps)
+        err = max(err, maxabs(host64(y[torch.from_numpy(c).cuda()]), ref))
+    note(f"modulate {w.name}: {len(rows)} rows, max-abs {err:.3e}")
     assert err <= TOL[w.dtype]
 
 
@@ -80,7 +86,7 @@ def test_modulate_wide_many_rows(w):
 
 @pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
 def test_modulate_full(w):
-    _modulate_case(w, sample_rows(w, per_seq=512) if w.tokens > 20000 else None)
+    _modulate_case(w)
 
 
 def _rope_case(w, rows=None):
@@ -94,16 +100,13 @@ def _rope_case(w, rows=None):
     torch.cuda.synchronize()
     ref_pos = o_grid.positions(w.cu_seqlens, *w.grid_hw)
     assert np.array_equal(pos.cpu().numpy().astype(np.int64), ref_pos), "position ids differ"
-    sel = slice(None) if rows is None else rows
-    rq = o_rope.apply_rope(inp["q"][sel], ref_pos[sel], w.rope_split, w.rope_base)
-    rk = o_rope.apply_rope(inp["k"][sel], ref_pos[sel], w.rope_split, w.rope_base)
-    if rows is None:
-        gq, gk = host64(q), host64(k)
-    else:
-        rt = torch.from_numpy(rows).cuda()
-        gq, gk = host64(q[rt]), host64(k[rt])
-    eq, ek = maxabs(gq, rq), maxabs(gk, rk)
-    note(f"rope {w.name}: max-abs q {eq:.3e} k {ek:.3e}")
+    rows = np.arange(w.tokens, dtype=np.int64) if rows is None else rows
+    eq = ek = 0.0
+    for c in _chunks(rows):
+        rt = torch.from_numpy(c).cuda()
+        eq = max(eq, maxabs(host64(q[rt]), o_rope.apply_rope(inp["q"][c], ref_pos[c], w.rope_split, w.rope_base)))
+        ek = max(ek, maxabs(host64(k[rt]), o_rope.apply_rope(inp["k"][c], ref_pos[c], w.rope_split, w.rope_base)))
+    note(f"rope {w.name}: {len(rows)} rows, max-abs q {eq:.3e} k {ek:.3e}")
     assert eq <= TOL[w.dtype] and ek <= TOL[w.dtype]
 
 
@@ -114,7 +117,7 @@ def test_rope_small(w):
 
 @pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
 def test_rope_full(w):
-    _rope_case(w, sample_rows(w, per_seq=512) if w.tokens > 20000 else None)
+    _rope_case(w)
 
 
 def test_rope_origin_is_identity_and_v_untouched():
@@ -229,3 +232,76 @@ def test_euler_per_frame_lands_on_data():
     dit.rf_euler_step(z, z, dev(u, w), dev((1.0 - t).astype(np.float32)), 1560)
     torch.cuda.synchronize()
     assert maxabs(host64(z), x1) <= 1e-4
+
+
+# ---- every kernel writes exactly its outputs (guard bands of canary values
+# around them keep their values) and is deterministic (a second run on the same
+# inputs gives the same bits): modulate, RoPE, the fused epilogue
+def _guarded(shape, dtype, fill=7.0, pad=4096):
+    """A tensor of `shape` inside a flat buffer with `pad` canary elements on each side."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + 2 * pad,), fill, dtype=dtype, device="cuda")
+    return buf, buf[pad:pad + n].view(shape), pad
+
+
+def _canaries_ok(buf, pad, fill=7.0):
+    return bool(torch.all(buf[:pad] == fill)) and bool(torch.all(buf[-pad:] == fill))
+
+
+GUARD = [synth.C1, SMALL[1], synth.custom("guard_wide", "bf16", (5, 9), (3, 2), 24, 128, (44, 42, 42),
+                                          tokens_per_row=45)]
+
+
+@pytest.mark.parametrize("w", GUARD, ids=lambda w: w.name)
+def test_modulate_guard_and_determinism(w):
+    need_gpu()
+    inp = synth.make(w, ["x", "gamma", "beta"])
+    x = dev(inp["x"], w)
+    outs = []
+    for _ in range(2):
+        buf, y, pad = _guarded(x.shape, x.dtype)
+        dit.dit_adaln_modulate(y, x, dev(inp["gamma"]), dev(inp["beta"]), w.tokens_per_row, w.eps)
+        torch.cuda.synchronize()
+        assert _canaries_ok(buf, pad)
+        outs.append(y.clone())
+    assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("w", GUARD, ids=lambda w: w.name)
+def test_rope_guard_and_determinism(w):
+    need_gpu()
+    inp = synth.make(w, ["q", "k"])
+    cu = None if w.dense else torch.from_numpy(w.cu_seqlens).cuda()
+    outs = []
+    for _ in range(2):
+        bq, q, pad = _guarded(inp["q"].shape, torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+        bk, k, _ = _guarded(inp["k"].shape, q.dtype)
+        q.copy_(dev(inp["q"], w))
+        k.copy_(dev(inp["k"], w))
+        bp, pos, _ = _guarded((w.tokens, 3), torch.int32, fill=-7)
+        dit.dit_rope3d(q, k, (w.frames[0], *w.grid_hw), w.rope_split, w.rope_base, cu_seqlens=cu,
+                       num_seqs=w.num_seqs, pos_out=pos)
+        torch.cuda.synchronize()
+        assert _canaries_ok(bq, pad) and _canaries_ok(bk, pad) and _canaries_ok(bp, pad, -7)
+        outs.append((q.clone(), k.clone(), pos.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("w", GUARD, ids=lambda w: w.name)
+def test_epilogue_guard_and_determinism(w):
+    need_gpu()
+    inp = synth.make(w, ["x", "alpha", "z", "u", "dt"])
+    br = dev(synth.make(w, ["v"])["v"].reshape(w.tokens, w.d_model), w)
+    x, z, u = dev(inp["x"], w), dev(inp["z"], w), dev(inp["u"], w)
+    outs = []
+    for _ in range(2):
+        bx, x_out, pad = _guarded(x.shape, x.dtype)
+        bz, z_out, _ = _guarded(z.shape, z.dtype)
+        dit.dit_gated_residual(x_out, x, br, dev(inp["alpha"]), w.tokens_per_row,
+                               euler=(z_out, z, u, dev(inp["dt"]), w.tokens_per_row))
+        torch.cuda.synchronize()
+        assert _canaries_ok(bx, pad) and _canaries_ok(bz, pad)
+        outs.append((x_out.clone(), z_out.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
