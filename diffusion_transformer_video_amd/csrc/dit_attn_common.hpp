@@ -267,6 +267,7 @@ inline hipError_t queue_device(QueueDevice*& out, int& dev) {
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     QueueDevice& d = g_queue_dev[dev];
+    std::lock_guard<std::mutex> g(d.mu);   // first use may come from several threads
     if (!d.init) {
         e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;

@@ -125,10 +125,12 @@ def test_full_size_one_whole_head(w):
     assert err <= TOL[w.dtype]
 
 
-# Launches with at least 4 work items per resident block take the persistent
-# path (one block per compute unit, items drawn from per-XCD queues); smaller
-# ones run one block per item. Every item is computed by the same code either
-# way, so a sequence's output cannot depend on which path ran it.
+# Launches with at least 4 work items per resident block (or 2, when one block
+# per item would leave its last round under 90% full) take the persistent path
+# (one block per compute unit, items drawn from per-XCD queues); smaller ones
+# run one block per item. An item the persistent launch does not split is
+# computed by the same code either way, so its output cannot depend on which
+# path ran it.
 PERSISTENT = [(128, 16), (64, 32)]   # (head_dim, heads): packed (8192, 300) takes the persistent path
 
 
@@ -151,13 +153,88 @@ def test_persistent_equals_per_item_launch(hd, heads):
     got_big = _run(big, inp)
     small = _seq_workload(f"pers{hd}_tail", "bf16", (300,), heads, hd)
     got_small = _run(small, {n: inp[n][8192:] for n in ("q", "k", "v")})
-    split_heads = set()
-    if hd == 128:
-        cus = torch.cuda.get_device_properties(0).multi_processor_count
-        split_heads = {item_rows(big, i)[0] for i in split_items(attn_items_total(big), cus)}
-    keep = [h for h in range(heads) if h not in split_heads]
+    keep = [h for h in range(heads) if h not in _split_heads(big)]
     assert keep
     assert np.array_equal(got_big[8192:, keep], got_small[:, keep])
+
+
+def _split_heads(w):
+    """Heads with an item that a persistent launch of w splits along the keys."""
+    if w.head_dim != 128:
+        return set()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return {item_rows(w, i)[0] for i in split_items(attn_items_total(w), cus)}
+
+
+def _same_launch(got, ref, split_heads):
+    """got against ref from another launch of the same call: bit for bit on heads
+    no launch form splits, within the bf16 bar on the others (a split item sums
+    its keys in pieces, a one-block-per-item launch in one pass)."""
+    keep = [h for h in range(got.shape[1]) if h not in split_heads]
+    if not torch.equal(got[:, keep], ref[:, keep]):
+        return False
+    cut = sorted(split_heads)
+    return not cut or float((got[:, cut].float() - ref[:, cut].float()).abs().max()) <= TOL["bf16"]
+
+
+def test_concurrent_streams():
+    """Eight streams issuing ten persistent-size launches each without waiting
+    for one another: 80 launches in flight against 64 queue-counter slots and
+    one split array, so some launches share nothing and run one block per item
+    or unsplit. Every output equals the launch run alone."""
+    need_gpu()
+    w = _seq_workload("pers_streams", "bf16", (8192, 300), 16, 128)
+    inp = synth.make(w, ["q", "k", "v"])
+    q, k, v = (dev(inp[n], w) for n in ("q", "k", "v"))
+    cu = torch.from_numpy(w.cu_seqlens).cuda()
+    ref = torch.empty_like(q)
+    dit.dit_attn3d(ref, q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen)
+    streams = [torch.cuda.Stream() for _ in range(8)]
+    outs = [[torch.empty_like(q) for _ in range(10)] for _ in streams]
+    torch.cuda.synchronize()
+    for r in range(10):
+        for s, o in zip(streams, outs):
+            with torch.cuda.stream(s):
+                dit.dit_attn3d(o[r], q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen)
+    torch.cuda.synchronize()
+    split_heads = _split_heads(w)
+    for i, o in enumerate(outs):
+        for r, x in enumerate(o):
+            assert _same_launch(x, ref, split_heads), (i, r)
+
+
+def test_graph_capture_replays():
+    """The call captured into a graph (under capture it runs one block per item,
+    which keeps no device state between launches) and replayed three times, with
+    eager launches of the same call between the replays: every replay equals the
+    eager output, and the eager launches stay bit-identical."""
+    need_gpu()
+    w = _seq_workload("pers_graph", "bf16", (8192, 300), 16, 128)
+    inp = synth.make(w, ["q", "k", "v"])
+    q, k, v = (dev(inp[n], w) for n in ("q", "k", "v"))
+    cu = torch.from_numpy(w.cu_seqlens).cuda()
+    ref = torch.empty_like(q)
+    dit.dit_attn3d(ref, q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen)
+    torch.cuda.synchronize()
+    o = torch.empty_like(q)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dit.dit_attn3d(o, q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen)
+    split_heads = _split_heads(w)
+    first = None
+    for r in range(3):
+        o.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same_launch(o, ref, split_heads), r
+        if first is None:
+            first = o.clone()
+        assert torch.equal(o, first), r
+        eager = torch.empty_like(q)
+        dit.dit_attn3d(eager, q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen)
+        torch.cuda.synchronize()
+        assert torch.equal(eager, ref), r
 
 
 def test_persistent_launch_many_sequences():
