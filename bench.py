@@ -248,15 +248,27 @@ def main():
         return max(2, min(16, -(-(1 << 30) // nbytes)))
 
     def timed_batch(fns):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for f in fns:
+        """Mean GPU time per launch of fns, launched back to back: captured once
+        into a graph and replayed, so that the host's per-call cost (argument
+        checks, ctypes) does not leave the GPU idle between kernels of ~20 us.
+        These kernels keep no device state between launches and make no memset,
+        so a replay is the same work as the eager calls."""
+        for f in fns:   # eager first: lazy setup stays out of the capture
             f()
-        e0.record()
-        for _ in range(2):
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
             for f in fns:
                 f()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(2):
+            g.replay()
         e1.record()
         torch.cuda.synchronize()
+        del g
         return e0.elapsed_time(e1) / (2 * len(fns))
 
     R = rotation(2 * w.tokens * w.d_model * esz)

@@ -164,7 +164,7 @@ int dit_rope3d(void* q, void* k, int64_t tokens, int32_t heads, int32_t head_dim
     if (k && overlaps(q, bytes, k, bytes)) return fail(DIT_E_INVAL, "%s: q and k overlap", fn);
     if (int rc = check_device(fn)) return rc;
     dit::RopeArgs a{q, k, tokens, heads, head_dim, grid_t, grid_h, grid_w, cu_seqlens, num_seqs,
-                    d_t, d_h, d_w, std::log2(base), pos_out};
+                    d_t, d_h, d_w, std::log2((double)base), pos_out};
     return launched(dit::launch_rope3d(a, dtype == DIT_BF16, (hipStream_t)stream), fn);
 }
 

@@ -278,8 +278,12 @@ inline hipError_t queue_device(QueueDevice*& out, int& dev) {
         if (e != hipSuccess) return e;
         e = hipGetSymbolAddress(reinterpret_cast<void**>(&d.split_cnt), HIP_SYMBOL(g_attn_split_cnt));
         if (e != hipSuccess) return e;
+        // The events only tell the host that a launch has finished with its
+        // counters and partials, which only kernels on this device read: no
+        // system-scope release (with one, each record wrote the L2 back and held
+        // the stream's next kernel ~10 us).
         for (int i = 0; i <= kQueueSlots; ++i) {
-            e = hipEventCreateWithFlags(&d.ev[i], hipEventDisableTiming);
+            e = hipEventCreateWithFlags(&d.ev[i], hipEventDisableTiming | hipEventDisableSystemFence);
             if (e != hipSuccess) return e;
         }
         d.init = true;

@@ -1,7 +1,14 @@
 // Device-side helpers shared by the gfx950 kernels: bf16 <-> fp32 packing,
-// 16-byte vector loads/stores of 8 activation values (stores are nontemporal:
-// every output of the bandwidth-bound kernels is written once and not re-read
-// by the same kernel), and wave reductions.
+// 16-byte vector loads/stores of 8 activation values, and wave reductions.
+// Activation loads and stores are nontemporal: every activation the
+// bandwidth-bound kernels touch is read once and written once per launch. The
+// loads matter as much as the stores: a cached load allocates the line in the
+// 256 MB memory-side cache, an in-place kernel (RoPE, the merge) then dirties
+// it there, and the next kernel pays for writing those lines back (measured:
+// modulate after RoPE 159 us instead of 117 us at the 480P video size; RoPE
+// back to back 238 us, 214 us with nontemporal loads). Parameter rows (gamma,
+// beta, alpha), which many tokens re-read, use cached loads (load_f32x8), and so
+// does the merge, where nontemporal loads measured 6% slower.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,7 +37,8 @@ struct Vec8;
 template <>
 struct Vec8<true> {
     __device__ __forceinline__ static void load(const void* base, int64_t idx8, float (&f)[8]) {
-        const uint4 w = reinterpret_cast<const uint4*>(base)[idx8];
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + idx8);
+        const uint4 w = make_uint4(v[0], v[1], v[2], v[3]);
         f[0] = bf16lo(w.x); f[1] = bf16hi(w.x); f[2] = bf16lo(w.y); f[3] = bf16hi(w.y);
         f[4] = bf16lo(w.z); f[5] = bf16hi(w.z); f[6] = bf16lo(w.w); f[7] = bf16hi(w.w);
     }
@@ -47,10 +55,10 @@ struct Vec8<true> {
 template <>
 struct Vec8<false> {
     __device__ __forceinline__ static void load(const void* base, int64_t idx8, float (&f)[8]) {
-        const float4* p = reinterpret_cast<const float4*>(base) + 2 * idx8;
-        const float4 a = p[0], b = p[1];
-        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+        const f32x4* p = reinterpret_cast<const f32x4*>(base) + 2 * idx8;
+        const f32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+        f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+        f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
     }
     __device__ __forceinline__ static void store(void* base, int64_t idx8, const float (&f)[8]) {
         f32x4* p = reinterpret_cast<f32x4*>(base) + 2 * idx8;
@@ -60,6 +68,14 @@ struct Vec8<false> {
         __builtin_nontemporal_store(b, p + 1);
     }
 };
+
+// 8 bf16 values through the caches (the merge's partial: a nontemporal load
+// measured slower there)
+__device__ __forceinline__ void load_bf16x8_cached(const void* base, int64_t idx8, float (&f)[8]) {
+    const uint4 w = reinterpret_cast<const uint4*>(base)[idx8];
+    f[0] = bf16lo(w.x); f[1] = bf16hi(w.x); f[2] = bf16lo(w.y); f[3] = bf16hi(w.y);
+    f[4] = bf16lo(w.z); f[5] = bf16hi(w.z); f[6] = bf16lo(w.w); f[7] = bf16hi(w.w);
+}
 
 __device__ __forceinline__ void load_f32x8(const float* base, int64_t idx8, float (&f)[8]) {
     const float4* p = reinterpret_cast<const float4*>(base) + 2 * idx8;
@@ -91,9 +107,17 @@ template <>
 struct Packed8<true> {
     uint4 w;
     __device__ __forceinline__ void load(const void* base, int64_t idx8) {
-        w = reinterpret_cast<const uint4*>(base)[idx8];
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + idx8);
+        w = make_uint4(v[0], v[1], v[2], v[3]);
     }
     __device__ __forceinline__ void zero() { w = make_uint4(0, 0, 0, 0); }
+    // Load of chunk idx8 if ok, else of chunk 0 (always in bounds; the caller
+    // ignores it). Branch-free: a load under a lane-divergent branch whose other
+    // side zeroes the registers makes the compiler wait for each such load
+    // before the next is issued.
+    __device__ __forceinline__ void load_or_first(const void* base, int64_t idx8, bool ok) {
+        load(base, ok ? idx8 : 0);
+    }
     // Empty asm that "redefines" the packed words: later passes unpack again
     // instead of the compiler keeping all unpacked floats live (emits nothing).
     __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w)); }
@@ -107,11 +131,15 @@ template <>
 struct Packed8<false> {
     float4 a, b;
     __device__ __forceinline__ void load(const void* base, int64_t idx8) {
-        const float4* p = reinterpret_cast<const float4*>(base) + 2 * idx8;
-        a = p[0];
-        b = p[1];
+        const f32x4* p = reinterpret_cast<const f32x4*>(base) + 2 * idx8;
+        const f32x4 x = __builtin_nontemporal_load(p), y = __builtin_nontemporal_load(p + 1);
+        a = make_float4(x[0], x[1], x[2], x[3]);
+        b = make_float4(y[0], y[1], y[2], y[3]);
     }
     __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ void load_or_first(const void* base, int64_t idx8, bool ok) {
+        load(base, ok ? idx8 : 0);
+    }
     __device__ __forceinline__ void refresh() {}
     __device__ __forceinline__ void unpack(float (&f)[8]) const {
         f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;

@@ -18,7 +18,7 @@ struct RopeArgs {
     void* q; void* k; int64_t tokens; int heads; int head_dim;
     int grid_t, grid_h, grid_w;
     const int32_t* cu_seqlens; int num_seqs;
-    int d_t, d_h, d_w; float log2_base;
+    int d_t, d_h, d_w; double log2_base;
     int32_t* pos_out;
 };
 hipError_t launch_rope3d(const RopeArgs& a, bool bf16, hipStream_t s);

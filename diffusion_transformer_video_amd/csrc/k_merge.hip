@@ -36,7 +36,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const float la = a.lse_acc[row], lb = a.lse_b[row];
     float oa[8], ob[8], res[8];
     load_f32x8(a.o_acc, gid, oa);
-    Vec8<BF16>::load(a.o_b, gid, ob);
+    if constexpr (BF16)
+        load_bf16x8_cached(a.o_b, gid, ob);
+    else
+        load_f32x8(reinterpret_cast<const float*>(a.o_b), gid, ob);
     const float m = fmaxf(la, lb);
     float lnew;
     if (m == -INFINITY) {

@@ -105,11 +105,13 @@ __global__ __launch_bounds__(64 * kWavesL) void modulate_lds_kernel(
     const int64_t row_chunk = tok * nchunk;
     const bool live = tok < tokens;
 
+    // unconditional loads (chunk 0 for idle lanes and rows past the end, never
+    // used): loads under a divergent branch are not kept in flight together
     Packed8<BF16> v[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = lane + 64 * i;
-        if (live && c < nchunk) v[i].load(x, row_chunk + c); else v[i].zero();
+        v[i].load_or_first(x, row_chunk + c, live && c < nchunk);
     }
     const int64_t last = (tok0 + kWavesL < tokens ? tok0 + kWavesL : tokens) - 1;
     const int64_t prow0 = tok0 / tokens_per_row;
@@ -129,10 +131,12 @@ __global__ __launch_bounds__(64 * kWavesL) void modulate_lds_kernel(
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        float f[8];
-        v[i].unpack(f);
+        if (lane + 64 * i < nchunk) {
+            float f[8];
+            v[i].unpack(f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s += f[e];
+            for (int e = 0; e < 8; ++e) s += f[e];
+        }
     }
     const float inv_d = 1.0f / (float)d_model;
     const float mean = wave_sum(s) * inv_d;
