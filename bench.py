@@ -248,27 +248,26 @@ def main():
         return max(2, min(16, -(-(1 << 30) // nbytes)))
 
     def timed_batch(fns):
-        """Mean GPU time per launch of fns, launched back to back: captured once
-        into a graph and replayed, so that the host's per-call cost (argument
-        checks, ctypes) does not leave the GPU idle between kernels of ~20 us.
-        These kernels keep no device state between launches and make no memset,
-        so a replay is the same work as the eager calls."""
-        for f in fns:   # eager first: lazy setup stays out of the capture
+        """Mean GPU time per launch of fns, launched back to back. A spin kernel
+        (torch.cuda._sleep) holds the stream while the host enqueues the timed
+        launches, so that they run with no idle gap between them: the host's
+        per-call cost (argument checks, ctypes; ~20 us) would otherwise leave the
+        GPU idle between kernels that take ~20 us themselves. The spin is sized
+        from the host's measured enqueue time and lies before the first event."""
+        t = time.perf_counter()
+        for f in fns:   # warm, and time the host's enqueue rate
             f()
+        host_s = time.perf_counter() - t
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for f in fns:
-                f()
-        g.replay()
-        torch.cuda.synchronize()
+        cycles = int(min(2e8, max(2e6, 2 * 2 * host_s * 2.5e9)))   # 2 rounds, 2x margin, >= 2.4 GHz
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(cycles)
         e0.record()
         for _ in range(2):
-            g.replay()
+            for f in fns:
+                f()
         e1.record()
         torch.cuda.synchronize()
-        del g
         return e0.elapsed_time(e1) / (2 * len(fns))
 
     R = rotation(2 * w.tokens * w.d_model * esz)
