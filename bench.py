@@ -122,14 +122,15 @@ class TimingEvent:
 
 def attn_kernel_name(w):
     """The bf16 attention kernel the library launches for this workload: the
-    persistent form from 4 query tiles (256 queries) per compute unit, or from 2
-    when one block per tile would leave the last round under 90% full (the rule
-    dit_attn3d documents); else one block per tile."""
+    persistent form on the whole chip (256 CUs) from 4 query tiles (256 queries)
+    per compute unit, or from 2 when one block per tile would leave the last
+    round under 90% full (the rule dit_attn3d documents); else one block per
+    tile."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     grid = -(-w.max_seqlen // 256) * w.heads * w.num_seqs
     last = grid % cus
-    pers = grid >= 4 * cus or (grid >= 2 * cus and last != 0 and 10 * last < 9 * cus)
+    pers = cus == 256 and (grid >= 4 * cus or (grid >= 2 * cus and last != 0 and 10 * last < 9 * cus))
     return "attn_bf16_persistent<128,8,1>" if pers else "attn_bf16_kernel<128,8,1>"
 
 

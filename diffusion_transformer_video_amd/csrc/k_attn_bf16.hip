@@ -73,8 +73,13 @@ constexpr float kLazyRescale = 8.0f;   // log2 headroom before the max is raised
 // full (the split tail fills it). Measured: 480P +0% / 720P +2% / one GPU's
 // Ulysses share (2.5 items per block) +10% against one block per item; the image
 // workload (3 whole rounds) is 6% faster with one block per item.
-__host__ __forceinline__ bool use_persistent(int64_t grid, int64_t resident) {
-    if (resident < 8) return false;
+//
+// Only on the whole chip (256 CUs, 8 XCDs): the queues are per XCD and a split
+// item's pieces are only taken on their own XCD (their partials never leave its
+// L2), so every XCD must run blocks of the launch. A partitioned device (fewer
+// XCDs) runs one block per item.
+__host__ __forceinline__ bool use_persistent(int64_t grid, int64_t resident, int cus) {
+    if (cus != 256 || resident < 8) return false;
     if (grid >= 4 * resident) return true;
     const int64_t last = grid % resident;
     return grid >= 2 * resident && last != 0 && 10 * last < 9 * resident;
@@ -885,7 +890,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, QB>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a, nqt);
         return hipGetLastError();
     };
-    if (use_persistent(grid, resident)) {
+    if (use_persistent(grid, resident, cus)) {
         // enough items per resident block for the queues (and the split tail) to
         // even out the XCDs
         return attn::persistent_launch(

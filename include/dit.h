@@ -135,7 +135,9 @@ int dit_rope3d(void* q, void* k, int64_t tokens, int32_t heads, int32_t head_dim
  * product rounded to bf16. float32 runs on the vector ALUs in full float32.
  * Launch forms. Let G be the number of query tiles (256 queries, 128 at
  * head_dim 64) times heads times sequences, and R the blocks the device holds at
- * once (one per compute unit; two at head_dim 64). With G >= 4R, or G >= 2R and a
+ * once (one per compute unit; two at head_dim 64). On the whole chip (256
+ * compute units in 8 XCDs; a partitioned device always takes one block per
+ * tile), with G >= 4R, or G >= 2R and a
  * last round of one-block-per-tile under 90% full, R persistent blocks draw
  * tiles from per-XCD queues (counters in library-owned device memory; a block
  * takes tiles of its own XCD first, then steals). At head_dim 128 the tiles of
