@@ -45,10 +45,11 @@
 //     The row sum accumulates the bf16-rounded probabilities the product uses.
 //   * Only the last key tile of a sequence carries a mask; rows past the end of
 //     the sequence are clamped on load and never stored.
-//   * Two launch forms run the same per-item code: one block per work item, or,
-//     for grids of at least 4 items per resident block, one persistent block per
-//     compute unit drawing items from per-XCD queues with stealing (the XCDs run
-//     at different clocks under this load; see dit_attn_common.hpp).
+//   * Two launch forms run the same per-item code: one block per work item, or
+//     (use_persistent below) one persistent block per compute unit drawing items
+//     from per-XCD queues with stealing (the XCDs run at different clocks under
+//     this load), whose last round is cut along the keys into pieces merged by
+//     the last piece to finish (see dit_attn_common.hpp).
 #include <math.h>
 
 #define DIT_ATTN_PERSISTENT
@@ -70,9 +71,10 @@ constexpr float kLazyRescale = 8.0f;   // log2 headroom before the max is raised
 // The persistent launch (per-XCD queues, split tail) is used from 4 work items
 // per resident block (the queues even out the XCDs' clock differences), and from
 // 2 when a one-block-per-item launch would leave its last round less than 90%
-// full (the split tail fills it). Measured: 480P +0% / 720P +2% / one GPU's
-// Ulysses share (2.5 items per block) +10% against one block per item; the image
-// workload (3 whole rounds) is 6% faster with one block per item.
+// full (the split tail fills it). Measured against the persistent launch
+// without the split tail: 720P +2%, one GPU's Ulysses share (2.5 items per
+// block) +8%, 480P within 1%; the image workload (3 whole rounds) runs 9% faster
+// with one block per item than persistent.
 //
 // Only on the whole chip (256 CUs, 8 XCDs): the queues are per XCD and a split
 // item's pieces are only taken on their own XCD (their partials never leave its
