@@ -135,12 +135,16 @@ def attn_kernel_name(w):
 
 
 def kernel_sha():
-    """Hash of the bf16 attention kernel's sources and its per-file compile flags:
-    hardware-counter figures belong to one build of the kernel."""
+    """Hash of the bf16 attention kernel's sources (comments and blank lines
+    dropped) and its per-file compile flags: hardware-counter figures belong to
+    one build of the kernel."""
+    import re
+
     from diffusion_transformer_video_amd import build as _build
     h = hashlib.sha256()
     for p in ATTN_SRCS:
-        h.update(open(p, "rb").read())
+        code = re.sub(r"//[^\n]*", "", open(p).read())
+        h.update("\n".join(l.rstrip() for l in code.splitlines() if l.strip()).encode())
     h.update(repr(_build.FILE_FLAGS.get("k_attn_bf16.hip", [])).encode())
     return h.hexdigest()[:16]
 
