@@ -118,7 +118,7 @@ __device__ __forceinline__ int items_total(const int32_t* cu_q, int num_seqs, in
 // round-robin over the 8 XCDs, so an XCD receives every 8th block; giving it a
 // contiguous range of items hands it whole heads with all their sequences
 // (balanced), and its concurrent blocks share one head's K/V in its L2.
-__device__ __forceinline__ void xcd_slice(int total, int x, int& start, int& len) {
+__host__ __device__ __forceinline__ void xcd_slice(int total, int x, int& start, int& len) {
     const int per = total / 8, rem = total % 8;
     len = per + (x < rem ? 1 : 0);
     start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
@@ -362,7 +362,7 @@ __device__ __forceinline__ int xcc_id() {
 // has its whole last round cut in halves: the XCDs' clock differences then
 // even out, by stealing, at half-item granularity. Ranges shorter than 2
 // rounds are left whole.
-__device__ __forceinline__ void split_plan(int len, int C, bool enabled, int& T, int& s) {
+__host__ __device__ __forceinline__ void split_plan(int len, int C, bool enabled, int& T, int& s) {
     T = 0;
     s = 1;
     if (!enabled || C > kSplitC || C <= 0 || len < 2 * C) return;
@@ -381,7 +381,7 @@ __device__ __forceinline__ void split_plan(int len, int C, bool enabled, int& T,
 }
 
 // Units of XCD x's queue: its full items, then T s pieces (piece-major).
-__device__ __forceinline__ int xcd_units(int len, int T, int s) { return len - T + T * s; }
+__host__ __device__ __forceinline__ int xcd_units(int len, int T, int s) { return len - T + T * s; }
 
 // The next unit for a block on XCD x: its own queue first, then the others in
 // turn. Returns the owning XCD v and the unit index u in its range, or v = -1
