@@ -248,6 +248,18 @@ def test_persistent_launch_many_sequences():
     _check(w, rows=sample_rows(w, per_seq=8, edge=2))
 
 
+def test_persistent_launch_with_few_items():
+    """The launch form is chosen from the grid bound (longest sequence x heads x
+    sequences), not the item count: one 8,192-token sequence and 63 one-token
+    sequences on one head give a grid of 2,048 (the persistent form) but only 95
+    work items, so most blocks find their XCD's queue empty at once and some
+    XCD ranges hold a dozen items. Every row against the oracle."""
+    lens = (8192,) + (1,) * 63
+    w = _seq_workload("pers_few", "bf16", lens, 1, 128, seed=41)
+    assert -(-max(lens) // 256) * w.heads * w.num_seqs >= 4 * 256
+    _check(w)
+
+
 def test_persistent_queue_slots_reused():
     """More persistent launches in a row than there are queue-counter slots (each
     launch's last block clears its slot for the next launch that uses it):
