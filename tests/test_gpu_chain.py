@@ -88,3 +88,54 @@ def test_block_identity_at_alpha_zero(w):
     inp = synth.make(w, ["x", "gamma", "beta", "alpha", "q", "k", "v", "z", "u", "dt"])
     x, _, _, x_out, _ = _gpu_step(w, inp, alpha=np.zeros_like(inp["alpha"]))
     assert torch.equal(x_out, x)
+
+
+def test_step_captured_in_a_graph_replays_bitwise():
+    """The whole step (modulate, RoPE in place on fresh copies of q and k,
+    attention, residual with the fused Euler update) captured into one graph and
+    replayed three times, with eager runs of the same step between the replays:
+    every replay's outputs equal the eager outputs bit for bit (no entry point of
+    the step keeps state between launches or records a memset; attention under
+    capture takes its one-block-per-item form, which is what the eager launch
+    takes at this size)."""
+    need_gpu()
+    w = CHAIN[1]
+    inp = synth.make(w, ["x", "gamma", "beta", "alpha", "q", "k", "v", "z", "u", "dt"])
+    x, q0, k0, v, z, u = (dev(inp[n], w) for n in ("x", "q", "k", "v", "z", "u"))
+    g, b, al, dt = dev(inp["gamma"]), dev(inp["beta"]), dev(inp["alpha"]), dev(inp["dt"])
+    cu = torch.from_numpy(w.cu_seqlens).cuda()
+    grid = (w.frames[0], *w.grid_hw)
+
+    def step(q, k, y, o, x_out, z_out):
+        q.copy_(q0)
+        k.copy_(k0)
+        dit.dit_adaln_modulate(y, x, g, b, w.tokens_per_row, w.eps)
+        dit.dit_rope3d(q, k, grid, w.rope_split, w.rope_base, cu_seqlens=cu, num_seqs=w.num_seqs)
+        dit.dit_attn3d(o, q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen)
+        dit.dit_gated_residual(x_out, x, o.view(w.tokens, w.d_model), al, w.tokens_per_row,
+                               euler=(z_out, z, u, dt, w.tokens_per_row))
+
+    def buffers():
+        return (torch.empty_like(q0), torch.empty_like(k0), torch.empty_like(x), torch.empty_like(q0),
+                torch.empty_like(x), torch.empty_like(z))
+
+    eager = buffers()
+    step(*eager)
+    torch.cuda.synchronize()
+    cap = buffers()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(*cap)
+    for r in range(3):
+        for t in cap:
+            t.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, e in zip(("q", "k", "y", "o", "x'", "z'"), cap, eager):
+            assert torch.equal(a, e), (r, name)
+        again = buffers()
+        step(*again)
+        torch.cuda.synchronize()
+        for a, e in zip(again, eager):
+            assert torch.equal(a, e), r
