@@ -113,8 +113,9 @@ int dit_adaln_modulate(void* y, const void* x, const float* gamma, const float* 
  *   head_dim % 8 == 0 and head_dim <= 256, heads >= 1
  * Accuracy: base^(-2j/d_a) / (2 pi) is computed in float64 and rounded to
  * float32; phi / (2 pi) = pos_a * that value is formed in float32 and its
- * fraction fed to the hardware sine/cosine of turns, so the angle carries a
- * relative error of ~2^-24 (plus ~1e-7 absolute): ~6e-6 rad at phi = 100.
+ * fraction fed to the hardware sine/cosine of turns (error ~1.3e-7), so the
+ * angle carries two float32 roundings, at most ~2^-23 relative: ~1.2e-5 rad at
+ * phi = 100 rad.
  */
 int dit_rope3d(void* q, void* k, int64_t tokens, int32_t heads, int32_t head_dim,
                int32_t grid_t, int32_t grid_h, int32_t grid_w,
