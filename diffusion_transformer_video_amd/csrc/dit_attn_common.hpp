@@ -246,12 +246,11 @@ __device__ uint32_t g_attn_queue[kQueueSlots][9 * kQWords];   // 8 XCD queues, t
 __device__ __attribute__((aligned(256))) SplitPartial g_attn_split[kSplitPieces];
 __device__ uint32_t g_attn_split_cnt[8 * kSplitC * kQWords];   // one counter (line) per split item
 
-// Per device: compute units, device addresses of the arrays, and the launch
-// tracking of the slots and the split scratch.
+// Per device: device addresses of the arrays, and the launch tracking of the
+// slots and the split scratch.
 struct QueueDevice {
     std::mutex mu;
     bool init = false;
-    int cus = 0;
     uint32_t* queue = nullptr;
     SplitPartial* split = nullptr;
     uint32_t* split_cnt = nullptr;
@@ -269,8 +268,6 @@ inline hipError_t queue_device(QueueDevice*& out, int& dev) {
     QueueDevice& d = g_queue_dev[dev];
     std::lock_guard<std::mutex> g(d.mu);   // first use may come from several threads
     if (!d.init) {
-        e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
         // the arrays' device addresses on this device (their names in host code are not)
         e = hipGetSymbolAddress(reinterpret_cast<void**>(&d.queue), HIP_SYMBOL(g_attn_queue));
         if (e != hipSuccess) return e;
@@ -292,15 +289,13 @@ inline hipError_t queue_device(QueueDevice*& out, int& dev) {
     return hipSuccess;
 }
 
-// Host: the current device's compute-unit count.
+// Host: the current device's compute-unit count (an attribute query only, so a
+// first call under stream capture creates nothing).
 inline hipError_t device_cus(int& cus) {
-    QueueDevice* d = nullptr;
     int dev = 0;
-    hipError_t e = queue_device(d, dev);
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> g(d->mu);
-    cus = d->cus;
-    return hipSuccess;
+    return hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
 }
 
 // true if resource i may be used by a launch on `stream` now
@@ -315,15 +310,17 @@ inline bool resource_free(QueueDevice& d, int i, hipStream_t stream) {
 // no slot is free, run `fallback()`. Serialised per device.
 template <class Persistent, class Fallback>
 inline hipError_t persistent_launch(hipStream_t stream, Persistent&& launch, Fallback&& fallback) {
+    // under capture first: replays would share device counters, and the state
+    // below (events, symbol addresses) is not created inside a capture
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return e;
+    if (cap != hipStreamCaptureStatusNone) return fallback();
     QueueDevice* dp = nullptr;
     int dev = 0;
-    hipError_t e = queue_device(dp, dev);
+    e = queue_device(dp, dev);
     if (e != hipSuccess) return e;
     QueueDevice& d = *dp;
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    e = hipStreamIsCapturing(stream, &cap);
-    if (e != hipSuccess) return e;
-    if (cap != hipStreamCaptureStatusNone) return fallback();   // replays would share device counters
     std::lock_guard<std::mutex> g(d.mu);
     int slot = -1;
     for (int t = 0; t < kQueueSlots; ++t) {
