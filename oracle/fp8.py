@@ -14,18 +14,31 @@ mantissa 7 is NaN. Encoding rounds to the nearest representable value, ties to
 an even mantissa.
 
 Readings taken here (the page gives none of these details):
-  * one scale per (tensor, head): amax_h = max |x[:, h, :]| over all tokens,
-    x is multiplied by 448 / amax_h (float32) so amax_h maps to 448, and the
-    dequantisation scale is amax_h / 448 (float32); an all-zero head keeps
-    scale 1 and codes 0;
-  * the float32 product x * (448 / amax_h) is what is rounded to E4M3 (the
+  * k and v: one scale per (tensor, head): amax_h = max |x[:, h, :]| over all
+    tokens, x is multiplied by 448 / amax_h (float32) so amax_h maps to 448,
+    and the dequantisation scale is amax_h / 448 (float32); an all-zero head
+    keeps scale 1 and codes 0;
+  * q: one scale per head too, chosen together with k's so that the score
+    scale -- the product of the two dequantisation scales and log2(e)/sqrt(d),
+    which turns code dot products into base-2 exponents of the softmax -- is a
+    power of two 2^n: n is the smallest integer with
+    2^n >= amax_q amax_k log2(e) / (448^2 sqrt(d)) (so the largest |q| maps
+    into (224, 448] rather than onto 448), decided in float64; q is multiplied
+    by g = amax_k log2(e) / (448 sqrt(d)) 2^-n (float64, rounded once to
+    float32) and the dequantisation scale is sq = 2^n sqrt(d) / (sk log2(e)),
+    sk = k's scale. When amax_q or amax_k is 0 every score is 0 whatever q
+    holds: q's codes are then 0, n = 0, sq = 1. n is kept in [-254, 254];
+  * the float32 product x * multiplier is what is rounded to E4M3 (the
     integer code is decided in float32, the precision the GPU path uses).
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 E4M3_MAX = 448.0
+N_MIN, N_MAX = -254, 254      # range of the score-scale exponent n
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -85,3 +98,49 @@ def quantize_per_head(x: np.ndarray):
 def dequantize(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     """codes [tokens, heads, hd], scale [heads] -> float64 values."""
     return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[None, :, None]
+
+
+def score_exponent(amax_q: float, amax_k: float, head_dim: int) -> int:
+    """The smallest integer n with 2^n >= amax_q amax_k log2(e) / (448^2
+    sqrt(head_dim)), decided in float64 (0 when either amax is 0), kept in
+    [N_MIN, N_MAX]."""
+    if amax_q == 0 or amax_k == 0:
+        return 0
+    t = np.float64(amax_q) * np.float64(amax_k) * (np.log2(np.e) / (E4M3_MAX * E4M3_MAX * np.sqrt(np.float64(head_dim))))
+    f, e = math.frexp(float(t))          # t = f 2^e, f in [0.5, 1)
+    n = e - 1 if f == 0.5 else e
+    return int(min(max(n, N_MIN), N_MAX))
+
+
+def quantize_q(q: np.ndarray, amax_k: np.ndarray):
+    """q [tokens, heads, d] (float32 values) and k's per-head amax ->
+    (codes uint8, amax_q [heads] float32, scale [heads] float64, n [heads] int64)
+    with scale_q * (amax_k / 448) * log2(e) / sqrt(d) = 2^n."""
+    q = np.asarray(q, dtype=np.float32)
+    heads, d = q.shape[1], q.shape[2]
+    amax = np.abs(q).max(axis=(0, 2)).astype(np.float32) if q.size else np.zeros(heads, np.float32)
+    amax_k = np.asarray(amax_k, dtype=np.float32)
+    codes = np.zeros(q.shape, dtype=np.uint8)
+    scale = np.ones(heads, dtype=np.float64)
+    n = np.zeros(heads, dtype=np.int64)
+    for h in range(heads):
+        if amax[h] == 0 or amax_k[h] == 0:
+            continue
+        n[h] = score_exponent(float(amax[h]), float(amax_k[h]), d)
+        g = np.float32(np.float64(amax_k[h]) * (np.log2(np.e) / (E4M3_MAX * np.sqrt(np.float64(d)))) * 2.0 ** -float(n[h]))
+        y = (q[:, h, :] * g).astype(np.float32)                 # float32 product
+        y = np.clip(y, -E4M3_MAX, E4M3_MAX)
+        codes[:, h, :] = e4m3_encode(y)
+        sk = np.float64(amax_k[h] / np.float32(E4M3_MAX))       # k's float32 scale
+        scale[h] = 2.0 ** float(n[h]) * np.sqrt(np.float64(d)) / (sk * np.log2(np.e))
+    return codes, amax, scale, n
+
+
+def quantize_qkv(q: np.ndarray, k: np.ndarray, v: np.ndarray):
+    """The three tensors of one FP8 attention: k and v by quantize_per_head, q by
+    quantize_q against k's amax. Returns (codes (q, k, v), amax [3, heads]
+    float32, scale [3, heads] float64, n [heads])."""
+    ck, ak, sk = quantize_per_head(k)
+    cv, av, sv = quantize_per_head(v)
+    cq, aq, sq, n = quantize_q(q, ak)
+    return (cq, ck, cv), np.stack([aq, ak, av]), np.stack([sq, sk.astype(np.float64), sv.astype(np.float64)]), n

@@ -43,7 +43,7 @@ def real_impl():
         interpolant_rows=o_epi.interpolant_rows, cfm_loss=o_epi.cfm_loss, midpoint_half=o_epi.midpoint_half,
         insert_frames=o_flow.insert_frames, frame_schedule=o_flow.frame_schedule,
         e4m3_encode=o_fp8.e4m3_encode, e4m3_decode=o_fp8.e4m3_decode, quantize_per_head=o_fp8.quantize_per_head,
-        dequantize=o_fp8.dequantize,
+        dequantize=o_fp8.dequantize, quantize_qkv=o_fp8.quantize_qkv,
     )
 
 
@@ -757,6 +757,47 @@ def pin_dequantize_per_head(impl):
         got = np.asarray(impl.dequantize(cc, sc))
         want = v * sc.astype(np.float64)[None, :, None] * np.ones((5, 3, 2))
         assert np.array_equal(got, want), hex(c)
+
+
+def pin_q_score_scale_power_of_two(impl):
+    """q's scale makes the score scale a power of two: for heads of very
+    different magnitudes (and tokens != heads != dims), sq * sk * log2(e) /
+    sqrt(d) equals 2^n with n an integer; it is the smallest such scale that
+    keeps q's codes inside E4M3 (the largest |q| / sq lies in (224, 448], so
+    2^(n-1) would overflow 448); every q element lies within half a code spacing
+    of its dequantised value; code dot products times 2^n are the dequantised
+    scores in base-2 units; k and v are quantised per head as on their own.
+    When k's head is all zero the scores are zero whatever q holds: q's codes
+    are 0 there; an all-zero q head also has codes 0."""
+    r = _rng(73)
+    d = 32
+    mq = np.array([1.0, 30.0, 1e-3, 2.0, 0.0], np.float32)
+    mk = np.array([1.0, 0.05, 500.0, 0.0, 1.0], np.float32)
+    x = [r.standard_normal((24, 5, d)).astype(np.float32) for _ in range(3)]
+    q, k, v = x[0] * mq[None, :, None], x[1] * mk[None, :, None], x[2]
+    (cq, ck, cv), amax, scale, n = impl.quantize_qkv(q, k, v)
+    ck2, ak2, sk2 = impl.quantize_per_head(k)
+    cv2, _, sv2 = impl.quantize_per_head(v)
+    assert np.array_equal(ck, ck2) and np.array_equal(cv, cv2)
+    assert np.array_equal(scale[1], sk2.astype(np.float64)) and np.array_equal(scale[2], sv2.astype(np.float64))
+    qd = np.asarray(impl.dequantize(cq, scale[0]))
+    kd = np.asarray(impl.dequantize(ck, scale[1]))
+    for h in range(5):
+        if mq[h] == 0 or mk[h] == 0:
+            assert np.all(cq[:, h, :] == 0)
+            continue
+        nh = int(n[h])
+        assert nh == n[h]
+        c = float(scale[0][h]) * float(scale[1][h]) * math.log2(math.e) / math.sqrt(d)
+        assert abs(c / 2.0 ** nh - 1.0) < 1e-13, (h, c, nh)
+        top = float(np.abs(q[:, h, :]).max()) / float(scale[0][h])
+        assert 224.0 * (1 - 1e-6) < top <= 448.0 * (1 + 1e-6), (h, top)
+        qh = q[:, h, :].astype(np.float64)
+        err = np.abs(qd[:, h, :] - qh)
+        assert np.all(err <= np.maximum(np.abs(qh) * 2.0 ** -4, 2.0 ** -10 * float(scale[0][h])) * (1 + 1e-6))
+        codes_dot = impl.e4m3_decode(cq[:, h, :]) @ impl.e4m3_decode(ck[:, h, :]).T
+        s2 = qd[:, h, :] @ kd[:, h, :].T * (math.log2(math.e) / math.sqrt(d))
+        assert np.allclose(codes_dot * 2.0 ** nh, s2, rtol=1e-12, atol=1e-300)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

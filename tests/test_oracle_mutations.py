@@ -205,6 +205,36 @@ def _dequant_over_dims(codes, scale):
     return fp8.e4m3_decode(codes) * np.asarray(scale, np.float64)[None, None, :]
 
 
+def _qkv_with(rule):
+    """quantize_qkv with q's scale chosen by another rule."""
+    def f(q, k, v):
+        from oracle import fp8
+        ck, ak, sk = fp8.quantize_per_head(k)
+        cv, av, sv = fp8.quantize_per_head(v)
+        q = np.asarray(q, np.float32)
+        d = q.shape[2]
+        aq = np.abs(q).max(axis=(0, 2)).astype(np.float32)
+        cq = np.zeros(q.shape, np.uint8)
+        sq = np.ones(q.shape[1])
+        n = np.zeros(q.shape[1], np.int64)
+        for h in range(q.shape[1]):
+            if aq[h] == 0 or ak[h] == 0:
+                continue
+            skh = float(ak[h] / np.float32(448))
+            if rule == "ignore_k":          # the k / v rule: amax -> 448
+                sq[h] = float(aq[h] / np.float32(448))
+                n[h] = int(np.floor(np.log2(sq[h] * skh * np.log2(np.e) / np.sqrt(d))))
+            else:
+                lg = np.log2(np.e) if rule == "floor" else 1.0     # "natural": no log2(e)
+                t = float(aq[h]) * float(ak[h]) * lg / (448.0 * 448.0 * np.sqrt(d))
+                n[h] = int(np.floor(np.log2(t))) if rule == "floor" else int(np.ceil(np.log2(t)))
+                sq[h] = 2.0 ** n[h] * np.sqrt(d) / (skh * lg)
+            y = np.clip((q[:, h, :] * np.float32(1.0 / sq[h])).astype(np.float32), -448, 448)
+            cq[:, h, :] = fp8.e4m3_encode(y)
+        return (cq, ck, cv), np.stack([aq, ak, av]), np.stack([sq, sk.astype(np.float64), sv.astype(np.float64)]), n
+    return f
+
+
 def _coords_swapped(n, gh, gw):
     n = np.asarray(n, dtype=np.int64)
     return np.stack([n // (gh * gw), n % gw, (n // gw) % gh], axis=-1)
@@ -266,6 +296,9 @@ MUTANTS = {
     "dequant_scale_is_amax": dict(dequantize=_dequant_by_amax),
     "dequant_scale_over_tokens": dict(dequantize=_dequant_over_tokens),
     "dequant_scale_over_dims": dict(dequantize=_dequant_over_dims),
+    "q_scale_ignores_k": dict(quantize_qkv=_qkv_with("ignore_k")),
+    "q_scale_exponent_floor": dict(quantize_qkv=_qkv_with("floor")),
+    "q_scale_natural_log": dict(quantize_qkv=_qkv_with("natural")),
     "grid_h_w_swapped": dict(coords=_coords_swapped),
     "interpolant_reversed": dict(interpolant=_interp_reversed),
     "euler_wrong_sign": dict(euler_step=_euler_minus),
