@@ -1,13 +1,16 @@
 // FP8 (OCP E4M3) attention on gfx950 matrix cores: both products on
-// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales), fp32 accumulation.
+// v_mfma_scale_f32_32x32x64_f8f6f4, fp32 accumulation.
 //
 // o = softmax(q k^T / sqrt(d_head)) v per (sequence, head) on the dequantised
 // values ("Por que e absurdamente dificil gerar um filme inteiro usando IA",
 // section "Matematica por tras"; the 8-bit quantisation of "DiT, Flow Matching e
 // 3D Attention", section "Engenharia de inferencia e paralelismo de contexto:
 // Ulysses, Ring Attention e FP8"). Inputs are the codes and per-head amax values
-// written by the quantisation kernel (k_quant_fp8.hip): dequantisation scales
-// amax / 448 fold into the exponent (q, k) and into the final normalisation (v).
+// written by the quantisation kernel (k_quant_fp8.hip). q's scale makes the
+// score scale (both dequantisation scales times log2(e) / sqrt(d)) a power of
+// two 2^n (dit_fp8.hpp), applied by the score product's E8M0 block scales: the
+// product's output is already the base-2 exponent of the softmax. v's scale
+// amax / 448 goes into the final normalisation.
 //
 // Same organisation as the bf16 kernel (8 waves x 32 queries per block, 64-key
 // tiles through 3-deep LDS rings loaded with direct HBM -> LDS loads, one
@@ -21,23 +24,29 @@
 //     transposed with exactly those keys at columns 32h + 16b + 4q + i, and
 //     the probabilities go from the score registers into the B operand with
 //     no lane exchange and no transposing read;
-//   * probabilities are exp2(s - m + 6) with the running max m raised whenever
-//     a tile max exceeds it by more than 2: the largest weight lies in
-//     [2^6, 2^8] (E4M3 holds up to 448), so weights down to 2^-12 of the
-//     largest keep E4M3's full 3-bit precision;
-//   * the exponentials alone take about as many cycles per tile as the
-//     products (one per score, each costing about two vector-ALU issue slots
-//     in a throughput probe), so the vector ALU is the bound and
-//     the rest of the softmax is kept off it: the row sums are one more
-//     product per tile, against a constant operand whose row 0 is 1.0 (they
-//     add the same E4M3 probabilities the output product uses); the tile loop
-//     is unrolled over the lcm of the 3-slot rings and the 2 score register
-//     sets, so LDS slot addresses are immediate offsets and no score register
-//     is copied.
+//   * probabilities are 2^(s - m + 6) with an integer running max m, raised to
+//     the ceiling of a tile max that exceeds it by more than 2: the largest
+//     weight lies in [2^5, 2^8] (E4M3 holds up to 448). The shift is applied by
+//     the conversion to E4M3: v_cvt_scalef32_pk_fp8_f32 divides by 2^(m - 6)
+//     (only the scale's exponent is used; probed: round to nearest even), so
+//     a score costs one exponential and half a conversion, no arithmetic. That
+//     needs 2^s itself in float32 range, i.e. m in [-100, 120] for every query
+//     of the block; an item whose max leaves that range is recomputed with the
+//     shift subtracted before the exponential (2^(s - m), conversion scale
+//     2^-6);
+//   * the exponentials take about as many cycles per tile as the products (one
+//     per score, each costing about two vector-ALU issue slots in a throughput
+//     probe), so the vector ALU is the bound and the rest of the softmax is
+//     kept off it: the row sums are one more product per tile, against a
+//     constant operand whose row 0 is 1.0 (they add the same E4M3
+//     probabilities the output product uses); the tile loop is unrolled over
+//     the lcm of the 3-slot rings and the 2 score register sets, so LDS slot
+//     addresses are immediate offsets and no score register is copied.
 #include <math.h>
 
 #include "dit_attn_common.hpp"
 #include "dit_device.hpp"
+#include "dit_fp8.hpp"
 #include "dit_internal.h"
 
 namespace dit {
@@ -55,6 +64,7 @@ constexpr int TILEB = BK * HD;       // bytes of a K tile (64 rows x 128) or a V
 constexpr float kLazy = 2.0f;        // log2 headroom before the max is raised
 constexpr float kPOffset = 6.0f;     // exp2 offset of the probabilities
 constexpr float kE4M3Max = 448.0f;
+constexpr float kFastMin = -100.0f, kFastMax = 120.0f;   // running max range of the unshifted exponentials
 
 // LDS swizzles of 16-byte chunks: K rows have 8 chunks, V^T rows 4. A 16-lane
 // group of an operand read takes 16 consecutive rows at one logical chunk; the
@@ -71,6 +81,10 @@ __device__ __forceinline__ i32x8 lds_op(uint32_t a0, uint32_t a1) {
 
 __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);   // e4m3 x e4m3, scale 1
+}
+// the same with the E8M0 block scale 2^(sb - 127) on B
+__device__ __forceinline__ f32x16 mfma8s(const i32x8& a, const i32x8& b, const f32x16& c, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
 }
 
 // max of the lane's 32 scores, a left-to-right chain (it compiles to 3-input
@@ -94,7 +108,9 @@ struct State {
     i32x8 ones;          // A operand whose row 0 is E4M3 1.0 at all 64 keys, rows 1..31 zero
     f32x16 O[4];
     f32x16 L;            // row sums: row 0 of L = ones x P (lanes of half 0, register 0)
-    float m_run, c;
+    float m_run;         // running max (an integer, or -inf before the first tile)
+    bool fast;           // wave-uniform: the unshifted exponentials are in range (max_update)
+    int scb;             // E8M0 block scale of the score product's Q operand: 2^n
 };
 
 // K tile (keys kbase..kbase+63): wave w moves rows 8w..8w+7 (1 KB); lane L
@@ -140,7 +156,7 @@ __device__ __forceinline__ void s_tile(State& p, uint32_t slot_off, f32x16 (&S)[
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const uint32_t off = slot_off + kb * 32 * HD;
-            S[kb] = mfma8(lds_op(ka[2 * i] + off, ka[2 * i + 1] + off), p.qreg[i], S[kb]);
+            S[kb] = mfma8s(lds_op(ka[2 * i] + off, ka[2 * i + 1] + off), p.qreg[i], S[kb], p.scb);
         }
 }
 
@@ -159,12 +175,15 @@ __device__ __forceinline__ void mask_tile(f32x16 (&S)[2], int g, int kbase, int 
     }
 }
 
-// raise the running max (rescaling O and l) when the tile max exceeds it by more
-// than kLazy -- a wave-uniform branch
+// raise the running max (rescaling O and l) to the ceiling of the tile max when
+// that exceeds it by more than kLazy -- a wave-uniform branch. The factor is a
+// power of two (integer maxima), so the rescale is exact. p.fast: every query
+// of the wave has its max in [kFastMin, kFastMax], where the unshifted
+// exponentials stay in float32 range.
 __device__ __forceinline__ void max_update(State& p, const f32x16 (&S)[2]) {
-    const float mxs = pair_max(max32(S)) * p.c;
+    const float mxs = pair_max(max32(S));
     if (__builtin_amdgcn_ballot_w64(mxs > p.m_run + kLazy) != 0) {
-        const float m_new = __builtin_fmaxf(p.m_run, mxs);
+        const float m_new = __builtin_fmaxf(p.m_run, __builtin_ceilf(mxs));
         const float alpha = __builtin_amdgcn_exp2f(p.m_run - m_new);
 #pragma unroll
         for (int r = 0; r < 16; ++r) p.L[r] *= alpha;
@@ -173,13 +192,19 @@ __device__ __forceinline__ void max_update(State& p, const f32x16 (&S)[2]) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) p.O[dt][r] *= alpha;
         p.m_run = m_new;
+        p.fast = __builtin_amdgcn_ballot_w64(!(m_new >= kFastMin && m_new <= kFastMax)) == 0;
     }
 }
 
 // probabilities of the tile in S as the B operand of O^T += V^T P^T (byte
-// 16b + r of the lane's 32 = score S[b][r])
+// 16b + r of the lane's 32 = score S[b][r]): E4M3(2^S / 2^(m - 6)) (FAST), or
+// with the shift subtracted first, E4M3(2^(S - m) / 2^-6) -- the same values
+// wherever the first form is in range
+template <bool FAST>
 __device__ __forceinline__ i32x8 probs(const State& p, const f32x16 (&S)[2]) {
-    const float off = kPOffset - p.m_run;
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    // 2^(m - 6) (m - 6 in [-106, 114] when FAST: a normal float), or 2^-6
+    const float pscale = FAST ? __int_as_float(((int)p.m_run - (int)kPOffset + 127) << 23) : 0x1p-6f;
     int w[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -187,17 +212,40 @@ __device__ __forceinline__ i32x8 probs(const State& p, const f32x16 (&S)[2]) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int j = 4 * t + e;
-            v[e] = __builtin_amdgcn_exp2f(fmaf(S[j >> 4][j & 15], p.c, off));
+            v[e] = __builtin_amdgcn_exp2f(FAST ? S[j >> 4][j & 15] : S[j >> 4][j & 15] - p.m_run);
         }
-        // the first conversion fills bytes 0-1 and keeps bytes 2-3 of its third
+        // the first conversion fills bytes 0-1 and keeps bytes 2-3 of its first
         // operand, which the second one overwrites: any register will do, and
         // v[0]'s (dead after it) spares a zeroing move
-        int d = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], __float_as_int(v[0]), false);
-        d = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], d, true);
-        w[t] = d;
+        s16x2 d = __builtin_bit_cast(s16x2, v[0]);
+        d = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(d, v[0], v[1], pscale, false);
+        d = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(d, v[2], v[3], pscale, true);
+        w[t] = __builtin_bit_cast(int, d);
     }
     const i32x8 r = {w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
     return r;
+}
+
+// P(j) from Sin and S(j+1) into Sout (the products are independent of the
+// exponentials, which the compiler interleaves with them), in the wave's mode.
+// The markers at both ends of each arm (empty asm, no instruction) keep the
+// common products from being hoisted or sunk out of the arms, away from the
+// exponentials they overlap.
+__device__ __forceinline__ i32x8 probs_and_scores(State& p, const f32x16 (&Sin)[2], uint32_t kslot,
+                                                  f32x16 (&Sout)[2]) {
+    i32x8 P;
+    if (p.fast) {
+        asm volatile("; fast probabilities");
+        P = probs<true>(p, Sin);
+        s_tile(p, kslot, Sout);
+        asm volatile("; fast probabilities end");
+    } else {
+        asm volatile("; shifted probabilities");
+        P = probs<false>(p, Sin);
+        s_tile(p, kslot, Sout);
+        asm volatile("; shifted probabilities end");
+    }
+    return P;
 }
 
 __device__ __forceinline__ void pv_tile(State& p, uint32_t slot_off, const i32x8& P) {
@@ -225,8 +273,7 @@ __device__ __forceinline__ void step(State& p, int j, const f32x16 (&Sin)[2], f3
     const bool ik = kn < p.ntiles, iv = vn < p.ntiles;
     if (ik) issue_k(p, kring[(J + 3) % ST], (uint32_t)kn * BK);
     if (iv) issue_v(p, vring[(J + 2) % ST], (uint32_t)vn);
-    const i32x8 P = probs(p, Sin);
-    s_tile(p, ((J + 1) % ST) * TILEB, Sout);   // S(j+1): independent of the probabilities above
+    const i32x8 P = probs_and_scores(p, Sin, ((J + 1) % ST) * TILEB, Sout);
     pv_tile(p, (J % ST) * TILEB, P);
     if (j + 1 == p.ntiles - 1) mask_tile(Sout, p.g, (j + 1) * BK, p.len);
     max_update(p, Sout);
@@ -248,8 +295,10 @@ __device__ __forceinline__ void step_rt(State& p, int j, f32x16 (&S)[2]) {
     const bool ik = kn < p.ntiles, iv = vn < p.ntiles;
     if (ik) issue_k(p, kring[kn % ST], (uint32_t)kn * BK);
     if (iv) issue_v(p, vring[vn % ST], (uint32_t)vn);
-    const i32x8 P = probs(p, S);
-    s_tile(p, (uint32_t)((j + 1) % ST) * TILEB, S);
+    f32x16 Sn[2];
+    const i32x8 P = probs_and_scores(p, S, (uint32_t)((j + 1) % ST) * TILEB, Sn);
+    S[0] = Sn[0];
+    S[1] = Sn[1];
     pv_tile(p, (uint32_t)(j % ST) * TILEB, P);
     if (j + 1 == p.ntiles - 1) mask_tile(S, p.g, (j + 1) * BK, p.len);
     max_update(p, S);
@@ -335,12 +384,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(AttnFp8Args a, int
 #pragma unroll
     for (int t = 0; t < 8; ++t) p.ones[t] = l32 == 0 ? 0x38383838 : 0;   // E4M3 1.0 = 0x38
     p.m_run = -INFINITY;
-    const float sq = a.amax[head] / kE4M3Max, sk = a.amax[a.heads + head] / kE4M3Max;
+    p.fast = false;   // set with the first tile's max
+    p.scb = 127 + fp8::score_exponent(a.amax[head], a.amax[a.heads + head]);   // score scale 2^n
     const float sv = a.amax[2 * a.heads + head] / kE4M3Max;
-    // log2(e) / sqrt(128); kept >= the smallest normal float so that a head whose q
-    // or k is all zero (scale 0) gets uniform weights rather than -inf * 0 on the
-    // masked keys (its true scores are all 0; this moves them by < 1e-30)
-    p.c = __builtin_fmaxf(sq * sk * (1.4426950408889634f / 11.313708498984761f), 1.17549435e-38f);
 
     // ---- prologue: K(0), V(0), K(1) resident; S(0) and its max; then the loads a
     // step -1 would have issued (K(2), V(1))
@@ -371,7 +417,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(AttnFp8Args a, int
     }
     for (; j < steps; ++j) step_rt(p, j, Sa);
     {
-        const i32x8 P = probs(p, Sa);
+        const i32x8 P = p.fast ? probs<true>(p, Sa) : probs<false>(p, Sa);
         pv_tile(p, (uint32_t)((p.ntiles - 1) % ST) * TILEB, P);
     }
 

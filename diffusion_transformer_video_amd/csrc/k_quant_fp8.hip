@@ -4,10 +4,13 @@
 // "DiT, Flow Matching e 3D Attention", section "Engenharia de inferencia e
 // paralelismo de contexto: Ulysses, Ring Attention e FP8", pairs
 // FlashAttention-3 with 8-bit floating point quantisation. One scale per
-// (tensor, head): amax_h = max |x[:, h, :]| maps to 448, the largest finite
-// E4M3 value; codes are x * (448 / amax_h) rounded to nearest even
+// (tensor, head). k and v: amax_h = max |x[:, h, :]| maps to 448, the largest
+// finite E4M3 value; codes are x * (448 / amax_h) rounded to nearest even
 // (v_cvt_pk_fp8_f32), clamped to +-448 first; the dequantisation scale is
-// amax_h / 448. An all-zero head gets codes 0.
+// amax_h / 448. q: its scale makes the score scale a power of two 2^n
+// (dit_fp8.hpp), so the attention kernel applies it as a matrix-core block
+// scale; its largest magnitude maps into (224, 448]. An all-zero head gets
+// codes 0.
 //
 // Layout written for the attention kernel:
 //   q8, k8  [tokens][heads][128] bytes, row-major like q and k;
@@ -23,6 +26,7 @@
 // LDS, one atomic max per block -- max is order independent, so the result is
 // deterministic); quantise (one block per (64-key tile, head)).
 #include "dit_device.hpp"
+#include "dit_fp8.hpp"
 #include "dit_internal.h"
 
 namespace dit {
@@ -126,7 +130,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantFp8Args a) {
         len = a.cu_seqlens[seq + 1] - a.cu_seqlens[seq];
     }
     const int n = min(64, len - 64 * j);   // keys in this tile (>= 1)
-    const float iq = inv_scale(a.amax[head]), ik = inv_scale(a.amax[a.heads + head]);
+    const float iq = fp8::q_multiplier(a.amax[head], a.amax[a.heads + head]);
+    const float ik = inv_scale(a.amax[a.heads + head]);
     const float iv = inv_scale(a.amax[2 * a.heads + head]);
     for (int i = threadIdx.x; i < HD * 64 / 16; i += kThreads) reinterpret_cast<uint4*>(vt)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();

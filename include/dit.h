@@ -298,9 +298,16 @@ int rf_cfm_loss(float* loss_tokens, float* loss_rows, const void* u, const void*
  * "Engenharia de inferencia e paralelismo de contexto: Ulysses, Ring Attention
  * e FP8", which pairs FlashAttention-3 with 8-bit quantisation). Format: OCP
  * E4M3 (bias 7, 3 mantissa bits, max 448, round to nearest even). One scale
- * per (tensor, head): amax[t][h] = max |x_t[:, h, :]|; codes =
- * E4M3(clamp(x * (448 / amax), +-448)); dequantised value = code * amax / 448;
- * an all-zero head has codes 0.
+ * per (tensor, head), amax[t][h] = max |x_t[:, h, :]|. k and v: codes =
+ * E4M3(clamp(x * (448 / amax), +-448)), dequantised value = code * amax / 448.
+ * q: its scale s_q makes the score scale s_q * s_k * log2(e) / sqrt(128) an
+ * exact power of two 2^n, n the smallest integer with
+ * 2^n >= amax_q * amax_k * log2(e) / (448^2 * sqrt(128)) (decided in float64,
+ * kept in [-127, 127]); codes = E4M3(clamp(q * g, +-448)) with the float32
+ * multiplier g = (float)(amax_k * log2(e) / (448 * sqrt(128)) * 2^-n), so the
+ * largest |q| maps into (224, 448], and s_q = 2^n * sqrt(128) / (s_k * log2(e)).
+ * An all-zero head has codes 0, and so has q's head when k's is all zero (its
+ * scores are 0 whatever q holds).
  *
  * dit_quant_fp8 writes
  *   q8, k8     [tokens][heads][128] uint8 codes (row-major like q, k)
@@ -314,7 +321,9 @@ int rf_cfm_loss(float* loss_tokens, float* loss_rows, const void* u, const void*
  *
  * dit_attn3d_fp8: o (bf16 [tokens][heads][128]) = softmax(q k^T / sqrt(128)) v
  * over the dequantised values, both products on E4M3 matrix cores with float32
- * accumulation; the probabilities enter the second product rounded to E4M3.
+ * accumulation (the score product scaled by 2^n, derived from amax as above);
+ * the probabilities enter the second product rounded to E4M3, as
+ * 2^(s - m + 6) with s the base-2 score and m an integer running maximum.
  * Sequences as dit_attn3d (dense: cu_seqlens NULL; packed: device offsets and
  * max_seqlen). head_dim must be 128. Outputs must not overlap inputs.
  */

@@ -27,7 +27,7 @@ Readings taken here (the page gives none of these details):
     by g = amax_k log2(e) / (448 sqrt(d)) 2^-n (float64, rounded once to
     float32) and the dequantisation scale is sq = 2^n sqrt(d) / (sk log2(e)),
     sk = k's scale. When amax_q or amax_k is 0 every score is 0 whatever q
-    holds: q's codes are then 0, n = 0, sq = 1. n is kept in [-254, 254];
+    holds: q's codes are then 0, n = 0, sq = 1. n is kept in [-127, 127];
   * the float32 product x * multiplier is what is rounded to E4M3 (the
     integer code is decided in float32, the precision the GPU path uses).
 """
@@ -38,7 +38,7 @@ import math
 import numpy as np
 
 E4M3_MAX = 448.0
-N_MIN, N_MAX = -254, 254      # range of the score-scale exponent n
+N_MIN, N_MAX = -127, 127      # range of the score-scale exponent n
 
 
 def e4m3_decode(codes) -> np.ndarray:

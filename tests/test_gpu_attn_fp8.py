@@ -6,11 +6,12 @@ the dequantised values.
 Tolerance of the attention (derived from the arithmetic; checked per element):
 the only rounding between the dequantised inputs and the float32 accumulators
 is the E4M3 rounding of the probabilities before the second product. In the
-kernel's units P_k = 2^(s_k log2 e - m + 6), the largest weight lies in
-[2^6, 2^8]; rounding to nearest moves P_k by d_k, at most half its spacing:
-2^-4 P_k for normal values, 2^-10 below 2^-6 (subnormals). Relative to the row
-total L = sum P that is |d_k| / L <= h_k = 2^-4 w_k + 2^-16 (w = the softmax
-weights). The kernel's row sum adds the same rounded values the product uses
+kernel's units P_k = 2^(s_k log2 e - m + 6) with an integer running max m
+(raised to the ceiling of a tile max that exceeds it by more than 2), the
+largest weight lies in [2^5, 2^8]; rounding to nearest moves P_k by d_k, at
+most half its spacing: 2^-4 P_k for normal values, 2^-10 below 2^-6
+(subnormals). Relative to the row total L = sum P >= 2^5 that is
+|d_k| / L <= h_k = 2^-4 w_k + 2^-15 (w = the softmax weights). The kernel's row sum adds the same rounded values the product uses
 (a product against a constant ones operand), so the output is
 sum (P_k + d_k) v_k / (L + D) with D = sum d_k, and its error is
     sum_k d_k (v_k - o) / (L + D)  =  [sum_k (d_k / L)(v_k - o)] / (1 + D / L).
@@ -59,13 +60,11 @@ def _check_quant(q, k, v, cu, q8, k8, v8t, amax):
     """Codes and amax exactly as the oracle's; V transposed with the tile
     permutation, sequences padded with zero codes to whole tiles."""
     heads = q.shape[1]
-    ref = [o_fp8.quantize_per_head(x) for x in (q, k, v)]
-    assert np.array_equal(q8.cpu().numpy(), ref[0][0]) and np.array_equal(k8.cpu().numpy(), ref[1][0])
-    got_amax = amax.cpu().numpy()
-    for t in range(3):
-        assert np.array_equal(got_amax[t], ref[t][1])
+    codes, ref_amax, _, _ = o_fp8.quantize_qkv(q, k, v)
+    assert np.array_equal(q8.cpu().numpy(), codes[0]) and np.array_equal(k8.cpu().numpy(), codes[1])
+    assert np.array_equal(amax.cpu().numpy(), ref_amax)
     vt = v8t.cpu().numpy()
-    vc = ref[2][0]
+    vc = codes[2]
     col = 0
     cu = np.asarray(cu, np.int64)
     perm = np.array([_vt_col(w) for w in range(64)])
@@ -96,7 +95,7 @@ def _fp8_bound(qd, kd, vd, cu, rows):
             S = qd[rows[sel], h, :] @ kd[lo:hi, h, :].T * scale
             w = np.exp(S - S.max(axis=1, keepdims=True))
             w /= w.sum(axis=1, keepdims=True)
-            hk = 2.0 ** -4 * w + 2.0 ** -16                                   # [rows, keys]
+            hk = 2.0 ** -4 * w + 2.0 ** -15                                   # [rows, keys]
             V = np.abs(vd[lo:hi, h, :])                                       # [keys, 128]
             oo = np.abs(o[sel, h, :])                                         # [rows, 128]
             # sum_k hk^2 (|v_k| + |o|)^2 = sum hk^2 v^2 + 2|o| sum hk^2 |v| + o^2 sum hk^2
@@ -113,8 +112,8 @@ def _run_case(q, k, v, cu, num_seqs, max_seqlen, rows=None, dense=False):
     o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
     dit.dit_attn3d_fp8(o, q8, k8, v8t, amax, None if dense else cut, num_seqs, max_seqlen)
     torch.cuda.synchronize()
-    refs = [o_fp8.quantize_per_head(x) for x in (q, k, v)]
-    qd, kd, vd = (o_fp8.dequantize(c, sc) for c, _, sc in refs)
+    codes, _, scales, _ = o_fp8.quantize_qkv(q, k, v)
+    qd, kd, vd = (o_fp8.dequantize(c, sc) for c, sc in zip(codes, scales))
     rows = np.arange(q.shape[0]) if rows is None else rows
     ref, tol = _fp8_bound(qd, kd, vd, cu, rows)
     got = o[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
@@ -186,15 +185,34 @@ def test_peaked_scores():
     _run_case(q, k, v, cu, 2, 500)
 
 
+def test_scores_beyond_the_unshifted_range():
+    """Running maxima outside [-100, 120] (base 2): every wave forms its
+    probabilities with the shift subtracted before the exponential -- a head
+    whose scores are all far above the range (q, k 40x larger), a head whose
+    scores are all far below it (every key nearly opposite its query), and a
+    head where the last keys' scores leave the range only late in the
+    sequence, so waves switch form in the middle of the key loop."""
+    need_gpu()
+    (q, k, v), cu = _inputs([700, 130], heads=3, seed=11)
+    q[:, 0, :] *= 40.0
+    k[:, 0, :] *= 40.0
+    u = np.ones(128, np.float32)
+    q[:, 1, :] = 3.0 * u + 0.3 * q[:, 1, :]
+    k[:, 1, :] = -3.0 * u + 0.3 * k[:, 1, :]
+    k[600:700, 2, :] *= 60.0
+    q, k = synth.bf16_round(q), synth.bf16_round(k)
+    _run_case(q, k, v, cu, 2, 700)
+
+
 @pytest.mark.parametrize("w", [synth.C2, synth.C3, synth.C4, synth.C5], ids=lambda w: w.name)
 def test_full_size_sampled_rows(w):
     need_gpu()
     (q, k, v), cu = _inputs(w)
     rows = sample_rows(w, per_seq=32, edge=4)
     q8, k8, v8t, amax = _run_case(q, k, v, cu, w.num_seqs, w.max_seqlen, rows=rows, dense=w.dense)
-    ref = [o_fp8.quantize_per_head(x) for x in (q, k, v)]
-    assert np.array_equal(amax.cpu().numpy()[0], ref[0][1])
-    assert np.array_equal(q8.cpu().numpy(), ref[0][0])
+    codes, ref_amax, _, _ = o_fp8.quantize_qkv(q, k, v)
+    assert np.array_equal(amax.cpu().numpy(), ref_amax)
+    assert np.array_equal(q8.cpu().numpy(), codes[0])
 
 
 def test_deterministic():
