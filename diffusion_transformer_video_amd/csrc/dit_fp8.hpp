@@ -24,20 +24,21 @@ namespace fp8 {
 constexpr double kScoreT = 0x1.5519f01ffd935p-21;   // log2(e) / (448 * 448 * sqrt(128))
 constexpr double kQMul = 0x1.2a76b21bfde0fp-12;     // log2(e) / (448 * sqrt(128))
 
-__device__ __forceinline__ int score_exponent(float amax_q, float amax_k) {
+// (host and device: a host program checks both against the oracle)
+__host__ __device__ inline int score_exponent(float amax_q, float amax_k) {
     if (!(amax_q > 0.f) || !(amax_k > 0.f)) return 0;
     const double t = ((double)amax_q * (double)amax_k) * kScoreT;   // a normal double
-    const uint64_t b = (uint64_t)__double_as_longlong(t);
+    const uint64_t b = __builtin_bit_cast(uint64_t, t);
     const int e = (int)((b >> 52) & 0x7ff) - 1023;                 // t = 1.f 2^e
     const int n = (b & 0xfffffffffffffull) != 0 ? e + 1 : e;
     return n < -127 ? -127 : (n > 127 ? 127 : n);
 }
 
 // q's float32 multiplier (0: codes 0)
-__device__ __forceinline__ float q_multiplier(float amax_q, float amax_k) {
+__host__ __device__ inline float q_multiplier(float amax_q, float amax_k) {
     if (!(amax_q > 0.f) || !(amax_k > 0.f)) return 0.f;
     const int n = score_exponent(amax_q, amax_k);
-    const double p2 = __longlong_as_double((long long)((uint64_t)(1023 - n) << 52));   // 2^-n, exact
+    const double p2 = __builtin_bit_cast(double, (uint64_t)(1023 - n) << 52);   // 2^-n, exact
     return (float)(((double)amax_k * kQMul) * p2);
 }
 

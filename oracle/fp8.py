@@ -112,6 +112,15 @@ def score_exponent(amax_q: float, amax_k: float, head_dim: int) -> int:
     return int(min(max(n, N_MIN), N_MAX))
 
 
+def q_multiplier(amax_q: float, amax_k: float, head_dim: int) -> np.float32:
+    """q's float32 multiplier g = amax_k log2(e) / (448 sqrt(head_dim)) 2^-n
+    (float64, rounded once to float32); 0 when either amax is 0."""
+    if amax_q == 0 or amax_k == 0:
+        return np.float32(0.0)
+    n = score_exponent(amax_q, amax_k, head_dim)
+    return np.float32(np.float64(amax_k) * (np.log2(np.e) / (E4M3_MAX * np.sqrt(np.float64(head_dim)))) * 2.0 ** -float(n))
+
+
 def quantize_q(q: np.ndarray, amax_k: np.ndarray):
     """q [tokens, heads, d] (float32 values) and k's per-head amax ->
     (codes uint8, amax_q [heads] float32, scale [heads] float64, n [heads] int64)
@@ -127,7 +136,7 @@ def quantize_q(q: np.ndarray, amax_k: np.ndarray):
         if amax[h] == 0 or amax_k[h] == 0:
             continue
         n[h] = score_exponent(float(amax[h]), float(amax_k[h]), d)
-        g = np.float32(np.float64(amax_k[h]) * (np.log2(np.e) / (E4M3_MAX * np.sqrt(np.float64(d)))) * 2.0 ** -float(n[h]))
+        g = q_multiplier(float(amax[h]), float(amax_k[h]), d)
         y = (q[:, h, :] * g).astype(np.float32)                 # float32 product
         y = np.clip(y, -E4M3_MAX, E4M3_MAX)
         codes[:, h, :] = e4m3_encode(y)
