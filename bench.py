@@ -165,7 +165,7 @@ def traffic_for(workload):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(sharding is a design note only); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
