@@ -286,6 +286,34 @@ def test_ulysses_share_shape():
     _check(w, rows=sample_rows(w, per_seq=64))
 
 
+def test_full_size_head_dim_64():
+    """The other supported head size at the 480P video workload's tokens and
+    d_model: 32,760 tokens x 80 heads x 64 (the persistent launch's 4-wave
+    blocks, two per CU). A row in every 256-query tile of every head, the
+    sequence edges and 2,048 seeded rows, all heads, against the oracle."""
+    w = synth.Workload("c3_hd64_80heads", "bf16", (30, 52), (21,), (32760,), 80, 64, (20, 22, 22),
+                       10000.0, 32760, 1113)
+    _check(w, rows=tile_rows(w))
+
+
+def test_full_size_peaked_scores():
+    """The 480P video workload with q and k four times larger (scores 16 times
+    larger: sharply peaked rows whose running max keeps rising, so the lazy
+    rescale runs throughout the persistent launch and its split tail), on a row
+    in every 256-query tile of every head, the edges and 2,048 seeded rows."""
+    need_gpu()
+    w = synth.C3
+    inp = synth.make(w, ["q", "k", "v"])
+    inp["q"] = synth.bf16_round(np.asarray(inp["q"], np.float32) * 4.0)
+    inp["k"] = synth.bf16_round(np.asarray(inp["k"], np.float32) * 4.0)
+    rows = tile_rows(w)
+    got = _run(w, inp, rows)
+    ref = o_attn.attention(inp["q"], inp["k"], inp["v"], w.cu_seqlens, rows=rows)
+    err = maxabs(got, ref)
+    note(f"attn {w.name}, q and k x4: max-abs {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
 def test_ones_values_and_identical_keys():
     need_gpu()
     w = _seq_workload("inv", "bf16", (777,), 2, 128)

@@ -215,6 +215,18 @@ def test_full_size_sampled_rows(w):
     assert np.array_equal(q8.cpu().numpy(), codes[0])
 
 
+def test_ulysses_share_shape():
+    """One GPU's share of the 480P video workload under head-sharded context
+    parallelism over 8 GPUs (5 heads x 32,760 tokens): 640 blocks, 2.5 per CU."""
+    need_gpu()
+    r = np.random.default_rng(1103)
+    T = 32760
+    q, k, v = (synth.bf16_round(r.standard_normal((T, 5, 128)).astype(np.float32)) for _ in range(3))
+    cu = np.array([0, T], np.int64)
+    w = synth.Workload("c3_share_5heads", "bf16", (30, 52), (21,), (32760,), 5, 128, (44, 42, 42), 10000.0, 32760, 1103)
+    _run_case(q, k, v, cu, 1, T, rows=sample_rows(w, per_seq=256, edge=8))
+
+
 def test_deterministic():
     need_gpu()
     (q, k, v), cu = _inputs([700, 64], heads=2, seed=7)
