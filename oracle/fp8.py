@@ -27,7 +27,10 @@ Readings taken here (the page gives none of these details):
     by g = amax_k log2(e) / (448 sqrt(d)) 2^-n (float64, rounded once to
     float32) and the dequantisation scale is sq = 2^n sqrt(d) / (sk log2(e)),
     sk = k's scale. When amax_q or amax_k is 0 every score is 0 whatever q
-    holds: q's codes are then 0, n = 0, sq = 1. n is kept in [-127, 127];
+    holds: q's codes are then 0, n = 0, sq = 1; likewise when n would lie
+    below -127 (every score below 2^-127 times the largest product of codes,
+    under 1e-31: uniform weights to float32 precision whatever q holds). Above
+    127, n is kept at 127;
   * the float32 product x * multiplier is what is rounded to E4M3 (the
     integer code is decided in float32, the precision the GPU path uses).
 """
@@ -38,7 +41,7 @@ import math
 import numpy as np
 
 E4M3_MAX = 448.0
-N_MIN, N_MAX = -127, 127      # range of the score-scale exponent n
+N_MIN, N_MAX = -127, 127      # range of the score-scale exponent n (below: q's codes 0)
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -100,22 +103,31 @@ def dequantize(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[None, :, None]
 
 
-def score_exponent(amax_q: float, amax_k: float, head_dim: int) -> int:
+def _exponent(amax_q: float, amax_k: float, head_dim: int) -> int:
     """The smallest integer n with 2^n >= amax_q amax_k log2(e) / (448^2
-    sqrt(head_dim)), decided in float64 (0 when either amax is 0), kept in
-    [N_MIN, N_MAX]."""
-    if amax_q == 0 or amax_k == 0:
-        return 0
+    sqrt(head_dim)), decided in float64."""
     t = np.float64(amax_q) * np.float64(amax_k) * (np.log2(np.e) / (E4M3_MAX * E4M3_MAX * np.sqrt(np.float64(head_dim))))
     f, e = math.frexp(float(t))          # t = f 2^e, f in [0.5, 1)
-    n = e - 1 if f == 0.5 else e
-    return int(min(max(n, N_MIN), N_MAX))
+    return e - 1 if f == 0.5 else e
+
+
+def q_codes_zero(amax_q: float, amax_k: float, head_dim: int) -> bool:
+    """q's codes are all 0: a zero amax, or every score below 2^-127 (n < N_MIN)."""
+    return amax_q == 0 or amax_k == 0 or _exponent(amax_q, amax_k, head_dim) < N_MIN
+
+
+def score_exponent(amax_q: float, amax_k: float, head_dim: int) -> int:
+    """The score-scale exponent n (module docstring): 0 when q's codes are all
+    0, at most N_MAX."""
+    if q_codes_zero(amax_q, amax_k, head_dim):
+        return 0
+    return int(min(_exponent(amax_q, amax_k, head_dim), N_MAX))
 
 
 def q_multiplier(amax_q: float, amax_k: float, head_dim: int) -> np.float32:
     """q's float32 multiplier g = amax_k log2(e) / (448 sqrt(head_dim)) 2^-n
-    (float64, rounded once to float32); 0 when either amax is 0."""
-    if amax_q == 0 or amax_k == 0:
+    (float64, rounded once to float32); 0 when q's codes are all 0."""
+    if q_codes_zero(amax_q, amax_k, head_dim):
         return np.float32(0.0)
     n = score_exponent(amax_q, amax_k, head_dim)
     return np.float32(np.float64(amax_k) * (np.log2(np.e) / (E4M3_MAX * np.sqrt(np.float64(head_dim)))) * 2.0 ** -float(n))
@@ -133,7 +145,7 @@ def quantize_q(q: np.ndarray, amax_k: np.ndarray):
     scale = np.ones(heads, dtype=np.float64)
     n = np.zeros(heads, dtype=np.int64)
     for h in range(heads):
-        if amax[h] == 0 or amax_k[h] == 0:
+        if q_codes_zero(float(amax[h]), float(amax_k[h]), d):
             continue
         n[h] = score_exponent(float(amax[h]), float(amax_k[h]), d)
         g = q_multiplier(float(amax[h]), float(amax_k[h]), d)

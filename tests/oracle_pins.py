@@ -768,12 +768,14 @@ def pin_q_score_scale_power_of_two(impl):
     of its dequantised value; code dot products times 2^n are the dequantised
     scores in base-2 units; k and v are quantised per head as on their own.
     When k's head is all zero the scores are zero whatever q holds: q's codes
-    are 0 there; an all-zero q head also has codes 0."""
+    are 0 there; an all-zero q head also has codes 0, and so has a head whose
+    scores all lie below 2^-127 (q and k of magnitude 1e-20: the exponent would
+    be below -127)."""
     r = _rng(73)
     d = 32
-    mq = np.array([1.0, 30.0, 1e-3, 2.0, 0.0], np.float32)
-    mk = np.array([1.0, 0.05, 500.0, 0.0, 1.0], np.float32)
-    x = [r.standard_normal((24, 5, d)).astype(np.float32) for _ in range(3)]
+    mq = np.array([1.0, 30.0, 1e-3, 2.0, 0.0, 1e-20], np.float32)
+    mk = np.array([1.0, 0.05, 500.0, 0.0, 1.0, 1e-20], np.float32)
+    x = [r.standard_normal((24, 6, d)).astype(np.float32) for _ in range(3)]
     q, k, v = x[0] * mq[None, :, None], x[1] * mk[None, :, None], x[2]
     (cq, ck, cv), amax, scale, n = impl.quantize_qkv(q, k, v)
     ck2, ak2, sk2 = impl.quantize_per_head(k)
@@ -782,9 +784,9 @@ def pin_q_score_scale_power_of_two(impl):
     assert np.array_equal(scale[1], sk2.astype(np.float64)) and np.array_equal(scale[2], sv2.astype(np.float64))
     qd = np.asarray(impl.dequantize(cq, scale[0]))
     kd = np.asarray(impl.dequantize(ck, scale[1]))
-    for h in range(5):
-        if mq[h] == 0 or mk[h] == 0:
-            assert np.all(cq[:, h, :] == 0)
+    for h in range(6):
+        if mq[h] == 0 or mk[h] == 0 or mq[h] < 1e-10:
+            assert np.all(cq[:, h, :] == 0) and n[h] == 0
             continue
         nh = int(n[h])
         assert nh == n[h]

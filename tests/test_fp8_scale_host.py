@@ -44,7 +44,9 @@ def test_exponent_and_multiplier_bit_exact(rows):
         assert struct.unpack("<I", struct.pack("<f", float(g)))[0] == gb, (aq, ak, float(g), _f(gb))
 
 
-def test_cases_cover_both_rounding_branches_and_the_clamps(rows):
+def test_cases_cover_the_range_ends(rows):
     ns = {n for _, _, n, _ in rows}
-    assert -127 in ns and 127 in ns            # both clamps reached
-    assert any(gb == 0 for *_, gb in rows)     # zero amax -> multiplier 0
+    assert 127 in ns                           # the upper clamp
+    assert any(gb == 0 and aqb == 0 for aqb, _, _, gb in rows)   # zero amax -> multiplier 0
+    # scores below 2^-127 (both amax nonzero): codes 0, n = 0
+    assert any(gb == 0 and n == 0 and aqb != 0 and akb != 0 for aqb, akb, n, gb in rows)

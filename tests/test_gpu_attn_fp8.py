@@ -215,6 +215,21 @@ def test_full_size_sampled_rows(w):
     assert np.array_equal(q8.cpu().numpy(), codes[0])
 
 
+def test_scores_below_the_exponent_range():
+    """q and k of magnitude 1e-20 in one head (every score below 2^-127 of the
+    largest code product): q's codes are 0 there, bit-exact with the oracle, and
+    each query gets the plain mean of its sequence's dequantised V rows."""
+    need_gpu()
+    (q, k, v), cu = _inputs([130, 65], heads=2, seed=12)
+    q[:, 1, :] *= 1e-20
+    k[:, 1, :] *= 1e-20
+    q, k = synth.bf16_round(q), synth.bf16_round(k)
+    q8, k8, v8t, amax, _ = _quant_gpu(q, k, v, cu, 2, 130)
+    _check_quant(q, k, v, cu, q8, k8, v8t, amax)
+    assert bool((q8[:, 1, :] == 0).all())
+    _run_case(q, k, v, cu, 2, 130)
+
+
 def test_ulysses_share_shape():
     """One GPU's share of the 480P video workload under head-sharded context
     parallelism over 8 GPUs (5 heads x 32,760 tokens): 640 blocks, 2.5 per CU."""

@@ -221,7 +221,11 @@ def _qkv_with(rule):
             if aq[h] == 0 or ak[h] == 0:
                 continue
             skh = float(ak[h] / np.float32(448))
-            if rule == "ignore_k":          # the k / v rule: amax -> 448
+            if rule == "clamp_low":         # exponents below -127 clamped instead of zero codes
+                t = float(aq[h]) * float(ak[h]) * np.log2(np.e) / (448.0 * 448.0 * np.sqrt(d))
+                n[h] = max(int(np.ceil(np.log2(t))), -127)
+                sq[h] = 2.0 ** n[h] * np.sqrt(d) / (skh * np.log2(np.e))
+            elif rule == "ignore_k":          # the k / v rule: amax -> 448
                 sq[h] = float(aq[h] / np.float32(448))
                 n[h] = int(np.floor(np.log2(sq[h] * skh * np.log2(np.e) / np.sqrt(d))))
             else:
@@ -299,6 +303,7 @@ MUTANTS = {
     "q_scale_ignores_k": dict(quantize_qkv=_qkv_with("ignore_k")),
     "q_scale_exponent_floor": dict(quantize_qkv=_qkv_with("floor")),
     "q_scale_natural_log": dict(quantize_qkv=_qkv_with("natural")),
+    "q_scale_clamps_tiny_exponent": dict(quantize_qkv=_qkv_with("clamp_low")),
     "grid_h_w_swapped": dict(coords=_coords_swapped),
     "interpolant_reversed": dict(interpolant=_interp_reversed),
     "euler_wrong_sign": dict(euler_step=_euler_minus),
