@@ -303,11 +303,12 @@ int rf_cfm_loss(float* loss_tokens, float* loss_rows, const void* u, const void*
  * q: its scale s_q makes the score scale s_q * s_k * log2(e) / sqrt(128) an
  * exact power of two 2^n, n the smallest integer with
  * 2^n >= amax_q * amax_k * log2(e) / (448^2 * sqrt(128)) (decided in float64,
- * kept in [-127, 127]); codes = E4M3(clamp(q * g, +-448)) with the float32
+ * kept at most 127); codes = E4M3(clamp(q * g, +-448)) with the float32
  * multiplier g = (float)(amax_k * log2(e) / (448 * sqrt(128)) * 2^-n), so the
  * largest |q| maps into (224, 448], and s_q = 2^n * sqrt(128) / (s_k * log2(e)).
  * An all-zero head has codes 0, and so has q's head when k's is all zero (its
- * scores are 0 whatever q holds).
+ * scores are 0 whatever q holds) or when n would lie below -127 (every score
+ * under 1e-31: uniform weights to float32 precision); n is then 0.
  *
  * dit_quant_fp8 writes
  *   q8, k8     [tokens][heads][128] uint8 codes (row-major like q, k)
