@@ -77,14 +77,32 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(QuantFp8Args a) {
     }
 }
 
+// A head's float32 multiplier, applied as (x * pre) * inv. k and v: 448 / amax,
+// except below amax = 2^-100, where that quotient can overflow: there x is
+// scaled by 2^64 first and the quotient taken of amax * 2^64 (both exact
+// power-of-two scalings, so the product is the same float32 value wherever the
+// plain form is finite). inv = 0: codes 0.
+struct Mul {
+    float pre, inv;
+};
+__device__ __forceinline__ Mul kv_multiplier(float amax) {
+    if (!(amax > 0.f)) return {1.f, 0.f};
+    if (amax < 0x1p-100f) return {0x1p64f, kE4M3Max / (amax * 0x1p64f)};
+    return {1.f, kE4M3Max / amax};
+}
+
 // 8 bf16 values (one 16-byte chunk) -> 8 E4M3 codes (as two dwords)
-__device__ __forceinline__ uint2 quant8(const uint4& w, float inv) {
-    if (inv == 0.f) return make_uint2(0, 0);   // all-zero head: codes 0
+__device__ __forceinline__ uint2 quant8(const uint4& w, Mul m) {
+    if (m.inv == 0.f) return make_uint2(0, 0);   // all-zero head: codes 0
     float f[8];
     f[0] = bf16lo(w.x); f[1] = bf16hi(w.x); f[2] = bf16lo(w.y); f[3] = bf16hi(w.y);
     f[4] = bf16lo(w.z); f[5] = bf16hi(w.z); f[6] = bf16lo(w.w); f[7] = bf16hi(w.w);
+    if (m.pre != 1.f) {   // block-uniform
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = fminf(fmaxf(f[e] * inv, -kE4M3Max), kE4M3Max);
+        for (int e = 0; e < 8; ++e) f[e] *= m.pre;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = fminf(fmaxf(f[e] * m.inv, -kE4M3Max), kE4M3Max);
     int lo = 0, hi = 0;
     lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], lo, false);
     lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
@@ -92,8 +110,6 @@ __device__ __forceinline__ uint2 quant8(const uint4& w, float inv) {
     hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
     return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
-
-__device__ __forceinline__ float inv_scale(float amax) { return amax > 0.f ? kE4M3Max / amax : 0.f; }
 
 // column of key w (0..63) of a tile in v8t (see the header)
 __device__ __forceinline__ int vt_col(int w) {
@@ -130,9 +146,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantFp8Args a) {
         len = a.cu_seqlens[seq + 1] - a.cu_seqlens[seq];
     }
     const int n = min(64, len - 64 * j);   // keys in this tile (>= 1)
-    const float iq = fp8::q_multiplier(a.amax[head], a.amax[a.heads + head]);
-    const float ik = inv_scale(a.amax[a.heads + head]);
-    const float iv = inv_scale(a.amax[2 * a.heads + head]);
+    const Mul iq = {1.f, fp8::q_multiplier(a.amax[head], a.amax[a.heads + head])};
+    const Mul ik = kv_multiplier(a.amax[a.heads + head]);
+    const Mul iv = kv_multiplier(a.amax[2 * a.heads + head]);
     for (int i = threadIdx.x; i < HD * 64 / 16; i += kThreads) reinterpret_cast<uint4*>(vt)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
     for (int idx = threadIdx.x; idx < 64 * (HD / 8); idx += kThreads) {

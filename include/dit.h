@@ -299,7 +299,9 @@ int rf_cfm_loss(float* loss_tokens, float* loss_rows, const void* u, const void*
  * e FP8", which pairs FlashAttention-3 with 8-bit quantisation). Format: OCP
  * E4M3 (bias 7, 3 mantissa bits, max 448, round to nearest even). One scale
  * per (tensor, head), amax[t][h] = max |x_t[:, h, :]|. k and v: codes =
- * E4M3(clamp(x * (448 / amax), +-448)), dequantised value = code * amax / 448.
+ * E4M3(clamp(x * (448 / amax), +-448)) in float32 (below amax = 2^-100 formed
+ * as (x * 2^64) * (448 / (amax * 2^64)): the same value wherever the plain form
+ * is finite), dequantised value = code * amax / 448.
  * q: its scale s_q makes the score scale s_q * s_k * log2(e) / sqrt(128) an
  * exact power of two 2^n, n the smallest integer with
  * 2^n >= amax_q * amax_k * log2(e) / (448^2 * sqrt(128)) (decided in float64,

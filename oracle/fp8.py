@@ -17,7 +17,10 @@ Readings taken here (the page gives none of these details):
   * k and v: one scale per (tensor, head): amax_h = max |x[:, h, :]| over all
     tokens, x is multiplied by 448 / amax_h (float32) so amax_h maps to 448,
     and the dequantisation scale is amax_h / 448 (float32); an all-zero head
-    keeps scale 1 and codes 0;
+    keeps scale 1 and codes 0. Below amax_h = 2^-100 the float32 quotient
+    448 / amax_h can overflow, so there the product is formed as
+    (x 2^64) (448 / (amax_h 2^64)): exact power-of-two scalings, the same
+    float32 value wherever the plain form is finite;
   * q: one scale per head too, chosen together with k's so that the score
     scale -- the product of the two dequantisation scales and log2(e)/sqrt(d),
     which turns code dot products into base-2 exponents of the softmax -- is a
@@ -90,8 +93,12 @@ def quantize_per_head(x: np.ndarray):
     for h in range(heads):
         if amax[h] == 0:
             continue
-        inv = np.float32(E4M3_MAX) / amax[h]                    # float32 division
-        y = (x[:, h, :] * inv).astype(np.float32)               # float32 product
+        if amax[h] < np.float32(2.0 ** -100):                   # pre-scaled: no overflow
+            inv = np.float32(E4M3_MAX) / (amax[h] * np.float32(2.0 ** 64))
+            y = ((x[:, h, :] * np.float32(2.0 ** 64)).astype(np.float32) * inv).astype(np.float32)
+        else:
+            inv = np.float32(E4M3_MAX) / amax[h]                # float32 division
+            y = (x[:, h, :] * inv).astype(np.float32)           # float32 product
         y = np.clip(y, -E4M3_MAX, E4M3_MAX)
         codes[:, h, :] = e4m3_encode(y)
         scale[h] = amax[h] / np.float32(E4M3_MAX)

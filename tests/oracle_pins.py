@@ -711,11 +711,12 @@ def o_fp8_values():
 def pin_quantize_per_head(impl):
     """Each head's largest magnitude maps to +-448 (0x7E / 0xFE); every value is
     within half a code spacing (relative 2^-4) of its dequantised value; an
-    all-zero head stays zero with scale 1."""
+    all-zero head stays zero with scale 1. Also for a head of magnitude 1e-37,
+    where the float32 quotient 448 / amax would overflow."""
     r = _rng(71)
-    x = r.standard_normal((40, 3, 16)).astype(np.float32) * np.array([1.0, 30.0, 0.0], np.float32)[None, :, None]
+    x = r.standard_normal((40, 4, 16)).astype(np.float32) * np.array([1.0, 30.0, 0.0, 1e-37], np.float32)[None, :, None]
     codes, amax, scale = impl.quantize_per_head(x)
-    for h in range(2):
+    for h in (0, 1, 3):
         i = np.unravel_index(np.argmax(np.abs(x[:, h, :])), x[:, h, :].shape)
         assert codes[i[0], h, i[1]] in (0x7E, 0xFE)
         deq = impl.e4m3_decode(codes[:, h, :]) * float(scale[h])

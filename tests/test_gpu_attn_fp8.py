@@ -230,6 +230,20 @@ def test_scores_below_the_exponent_range():
     _run_case(q, k, v, cu, 2, 130)
 
 
+def test_tiny_k_and_v_heads():
+    """A k head and a v head of magnitude 1e-37, where the float32 quotient
+    448 / amax would overflow (the multiplier is then formed pre-scaled): codes
+    bit-exact with the oracle, attention against it."""
+    need_gpu()
+    (q, k, v), cu = _inputs([130, 65], heads=3, seed=13)
+    k[:, 1, :] *= 1e-37
+    v[:, 2, :] *= 1e-37
+    k, v = synth.bf16_round(k), synth.bf16_round(v)
+    q8, k8, v8t, amax, _ = _quant_gpu(q, k, v, cu, 2, 130)
+    _check_quant(q, k, v, cu, q8, k8, v8t, amax)
+    _run_case(q, k, v, cu, 2, 130)
+
+
 def test_ulysses_share_shape():
     """One GPU's share of the 480P video workload under head-sharded context
     parallelism over 8 GPUs (5 heads x 32,760 tokens): 640 blocks, 2.5 per CU."""
