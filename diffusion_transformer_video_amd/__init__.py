@@ -26,7 +26,7 @@ DIT_F32, DIT_BF16 = 0, 1
 DIT_OK, DIT_E_INVAL, DIT_E_UNSUPPORTED, DIT_E_HIP = 0, 1, 2, 3
 
 EXPORTS = ("dit_last_error", "dit_version", "dit_adaln_modulate", "dit_rope3d",
-           "dit_attn3d", "dit_attn3d_lse", "dit_attn_merge", "dit_gated_residual", "rf_euler_step",
+           "dit_attn3d", "dit_attn3d_noalloc", "dit_attn3d_lse", "dit_attn_merge", "dit_gated_residual", "rf_euler_step",
            "rf_midpoint_half", "rf_interpolant", "rf_cfm_loss", "flow_insert_frames",
            "flow_frame_schedule", "dit_fp8_v_stride", "dit_quant_fp8", "dit_attn3d_fp8")
 
@@ -64,8 +64,9 @@ def lib() -> ctypes.CDLL:
         L.dit_rope3d.restype = ctypes.c_int
         L.dit_rope3d.argtypes = [vp, vp, i64, i32, i32, i32, i32, i32, vp, i32,
                                  i32, i32, i32, f32, vp, i32, vp]
-        L.dit_attn3d.restype = ctypes.c_int
-        L.dit_attn3d.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, vp]
+        for name in ("dit_attn3d", "dit_attn3d_noalloc"):
+            getattr(L, name).restype = ctypes.c_int
+            getattr(L, name).argtypes = [vp, vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, vp]
         L.dit_attn3d_lse.restype = ctypes.c_int
         L.dit_attn3d_lse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, vp, vp, i32, i32, i32, i32, vp]
         L.dit_attn_merge.restype = ctypes.c_int
@@ -191,9 +192,7 @@ def dit_rope3d(q, k, grid: Sequence[int], split: Sequence[int], base: float = 10
     return q, k
 
 
-def dit_attn3d(o, q, k, v, cu_seqlens=None, num_seqs: int = 1, max_seqlen: int = 0, stream=None):
-    """o = softmax(q k^T / sqrt(head_dim)) v per (sequence, head); all [tokens, heads, hd].
-    cu_seqlens: None (dense, num_seqs equal sequences) or device int32 [num_seqs + 1]."""
+def _attn3d(entry, o, q, k, v, cu_seqlens, num_seqs, max_seqlen, stream):
     _offsets(("cu_seqlens", cu_seqlens))
     _dev(o, q, k, v, cu_seqlens)
     if q.dim() != 3 or any(t.shape != q.shape or t.dtype != q.dtype for t in (k, v, o)):
@@ -201,10 +200,22 @@ def dit_attn3d(o, q, k, v, cu_seqlens=None, num_seqs: int = 1, max_seqlen: int =
     tokens, heads, hd = q.shape
     if cu_seqlens is not None:
         num_seqs = cu_seqlens.numel() - 1
-    _check(lib().dit_attn3d(_ptr(o), _ptr(q), _ptr(k), _ptr(v), tokens, heads, hd,
-                            _ptr(cu_seqlens), int(num_seqs), int(max_seqlen), _dtype_code(q),
-                            _stream(stream)))
+    _check(getattr(lib(), entry)(_ptr(o), _ptr(q), _ptr(k), _ptr(v), tokens, heads, hd,
+                                 _ptr(cu_seqlens), int(num_seqs), int(max_seqlen), _dtype_code(q),
+                                 _stream(stream)))
     return o
+
+
+def dit_attn3d(o, q, k, v, cu_seqlens=None, num_seqs: int = 1, max_seqlen: int = 0, stream=None):
+    """o = softmax(q k^T / sqrt(head_dim)) v per (sequence, head); all [tokens, heads, hd].
+    cu_seqlens: None (dense, num_seqs equal sequences) or device int32 [num_seqs + 1]."""
+    return _attn3d("dit_attn3d", o, q, k, v, cu_seqlens, num_seqs, max_seqlen, stream)
+
+
+def dit_attn3d_noalloc(o, q, k, v, cu_seqlens=None, num_seqs: int = 1, max_seqlen: int = 0, stream=None):
+    """dit_attn3d without any allocation at call time (the library's fixed scratch slot;
+    calls that overlap on one device race). Arguments as dit_attn3d."""
+    return _attn3d("dit_attn3d_noalloc", o, q, k, v, cu_seqlens, num_seqs, max_seqlen, stream)
 
 
 def dit_attn3d_lse(o, lse, q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, num_seqs: int = 1,

@@ -174,7 +174,7 @@ namespace {
 int attn_common(const char* fn, void* o, float* lse, const void* q, const void* k, const void* v,
                 int64_t tokens_q, int64_t tokens_k, int32_t heads, int32_t head_dim,
                 const int32_t* cu_q, const int32_t* cu_k, int32_t num_seqs,
-                int32_t max_q, int32_t max_k, int32_t dtype, void* stream) {
+                int32_t max_q, int32_t max_k, int32_t dtype, void* stream, bool noalloc = false) {
     if (int rc = check_dtype(dtype, fn)) return rc;
     if (!o || !q || !k || !v) return fail(DIT_E_INVAL, "%s: NULL pointer argument", fn);
     if (tokens_q <= 0 || tokens_k <= 0) return fail(DIT_E_INVAL, "%s: token counts must be > 0", fn);
@@ -221,8 +221,9 @@ int attn_common(const char* fn, void* o, float* lse, const void* q, const void* 
     dit::AttnArgs a{o, q, k, v, tokens_q, heads, head_dim, cu_q, num_seqs, seq_q,
                     (float)(1.4426950408889634 / std::sqrt((double)head_dim)),
                     (float)(1.0 / std::sqrt((double)head_dim)), cu_k, seq_k, lse};
-    hipError_t e = dtype == DIT_BF16 ? dit::launch_attn3d_bf16(a, (hipStream_t)stream)
-                                     : dit::launch_attn3d_f32(a, (hipStream_t)stream);
+    hipError_t e = dtype != DIT_BF16 ? dit::launch_attn3d_f32(a, (hipStream_t)stream)
+                   : noalloc         ? dit::launch_attn3d_bf16_noalloc(a, (hipStream_t)stream)
+                                     : dit::launch_attn3d_bf16(a, (hipStream_t)stream);
     return launched(e, fn);
 }
 
@@ -234,6 +235,14 @@ int dit_attn3d(void* o, const void* q, const void* k, const void* v,
                int32_t dtype, void* stream) {
     return attn_common("dit_attn3d", o, nullptr, q, k, v, tokens, tokens, heads, head_dim, cu_seqlens,
                        cu_seqlens, num_seqs, max_seqlen, max_seqlen, dtype, stream);
+}
+
+int dit_attn3d_noalloc(void* o, const void* q, const void* k, const void* v,
+                       int64_t tokens, int32_t heads, int32_t head_dim,
+                       const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                       int32_t dtype, void* stream) {
+    return attn_common("dit_attn3d_noalloc", o, nullptr, q, k, v, tokens, tokens, heads, head_dim, cu_seqlens,
+                       cu_seqlens, num_seqs, max_seqlen, max_seqlen, dtype, stream, true);
 }
 
 int dit_attn3d_lse(void* o, float* lse, const void* q, const void* k, const void* v,

@@ -37,6 +37,9 @@ struct AttnArgs {
     float* lse;                  // NULL, or [tokens, heads]: ln sum_keys exp(q.k / sqrt(d))
 };
 hipError_t launch_attn3d_bf16(const AttnArgs& a, hipStream_t s);
+// the same arithmetic; persistent launches use the file's static scratch slot
+// (no launch tracking, no split tail)
+hipError_t launch_attn3d_bf16_noalloc(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn3d_f32(const AttnArgs& a, hipStream_t s);
 
 // (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_b, lse_b)); o_acc fp32.

@@ -877,8 +877,52 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1) void attn_bf
     }
 }
 
+// ---- Scratch of the allocation-free entry point (dit_attn3d_noalloc): one
+// persistent-launch queue slot -- the 8 XCD counters and the finished-block
+// count, a 64-byte line each, 576 bytes -- in a file-scope device array (one copy
+// per device, kept until the process ends). The name is a host-side stand-in:
+// host code uses only the per-device address that hipGetSymbolAddress returns.
+// The counters count work items, so no input needs more than this. Every
+// allocation-free call on a device shares the slot: calls that overlap on one
+// device race (their blocks would draw each other's items).
+constexpr int kScratchWords = 9 * attn::kQWords;
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+struct ScratchDevice {
+    std::mutex mu;
+    bool init = false;
+    uint32_t* ptr = nullptr;
+};
+ScratchDevice g_scratch_dev[64];
+
+// The current device's address of `scratch`, resolved on its first use.
+hipError_t scratch_address(uint32_t*& out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    ScratchDevice& d = g_scratch_dev[dev];
+    std::lock_guard<std::mutex> g(d.mu);
+    if (!d.init) {
+        e = hipGetSymbolAddress(reinterpret_cast<void**>(&d.ptr), HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        d.init = true;
+    }
+    out = d.ptr;
+    return hipSuccess;
+}
+
+// Zeroes the queue slot before a launch (a kernel, not a memset node, so a
+// captured graph clears it on every replay too).
+__global__ void scratch_clear_kernel(uint32_t* q, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) q[i] = 0u;
+}
+
+// noalloc: persistent launches take their queue slot from `scratch` (no launch
+// tracking, no split tail); otherwise from the tracked slots of
+// dit_attn_common.hpp, with the split tail when its scratch is free.
 template <int HD, int NW, int QB>
-hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_t(const AttnArgs& a, hipStream_t s, bool noalloc) {
     constexpr int BQ = 32 * QB * NW;
     const int nqt = (a.max_seqlen + BQ - 1) / BQ;
     const int64_t grid = (int64_t)nqt * a.heads * a.num_seqs;   // >= the number of items
@@ -895,6 +939,17 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     if (use_persistent(grid, resident, cus)) {
         // enough items per resident block for the queues (and the split tail) to
         // even out the XCDs
+        if (noalloc) {
+            uint32_t* q = nullptr;
+            e = scratch_address(q);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(scratch_clear_kernel, dim3(1), dim3(64), 0, s, q, kScratchWords);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const AttnLaunch L{a, nqt, (int)resident, q, nullptr, nullptr};
+            hipLaunchKernelGGL((attn_bf16_persistent<HD, NW, QB>), dim3((unsigned)resident), dim3(64 * NW), 0, s, L);
+            return hipGetLastError();
+        }
         return attn::persistent_launch(
             s,
             [&](uint32_t* queue, attn::SplitPartial* split, uint32_t* split_cnt) -> hipError_t {
@@ -911,8 +966,13 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn3d_bf16(const AttnArgs& a, hipStream_t s) {
-    if (a.head_dim == 64) return launch_t<64, 4, 1>(a, s);
-    return launch_t<128, 8, 1>(a, s);
+    if (a.head_dim == 64) return launch_t<64, 4, 1>(a, s, false);
+    return launch_t<128, 8, 1>(a, s, false);
+}
+
+hipError_t launch_attn3d_bf16_noalloc(const AttnArgs& a, hipStream_t s) {
+    if (a.head_dim == 64) return launch_t<64, 4, 1>(a, s, true);
+    return launch_t<128, 8, 1>(a, s, true);
 }
 
 }  // namespace dit

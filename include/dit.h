@@ -166,6 +166,25 @@ int dit_attn3d(void* o, const void* q, const void* k, const void* v,
                int32_t dtype, void* stream);
 
 /*
+ * dit_attn3d for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments,
+ * validation, arithmetic and results as dit_attn3d; it calls no hipMalloc,
+ * hipFree, event or other allocating routine. Its persistent launches (same
+ * rule as dit_attn3d) take their queue counters from one fixed slot of a
+ * library-owned device array of 576 bytes per device (resolved with
+ * hipGetSymbolAddress on the first call on each device, kept until the process
+ * ends, cleared by a kernel before every launch) and never cut tiles along their
+ * keys, so no input needs more scratch than that; every tile's result is bitwise
+ * that of an unsplit dit_attn3d tile. All calls on one device share the slot:
+ * calls that overlap on one device (several streams, concurrent replays of
+ * graphs that captured it) race and may skip or repeat tiles. Serialise them.
+ */
+int dit_attn3d_noalloc(void* o, const void* q, const void* k, const void* v,
+                       int64_t tokens, int32_t heads, int32_t head_dim,
+                       const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                       int32_t dtype, void* stream);
+
+/*
  * One ring-attention step ("DiT, Flow Matching e 3D Attention", section
  * "Engenharia de inferencia e paralelismo de contexto: Ulysses, Ring Attention e
  * FP8"): each sequence's queries attend to that sequence's key/value block, and

@@ -90,6 +90,20 @@ def test_attn_validation():
     assert L.dit_attn3d(o, q, k, v, 0, 2, 128, None, 1, 0, 1, None) == dit.DIT_E_INVAL
 
 
+def test_attn_noalloc_validation():
+    """The allocation-free entry point validates exactly as dit_attn3d, under its own name."""
+    L = ensure_built()
+    o, q, k, v = FAKE * 16, FAKE, FAKE * 4, FAKE * 8
+    assert L.dit_attn3d_noalloc(None, q, k, v, 64, 2, 128, None, 1, 0, 1, None) == dit.DIT_E_INVAL
+    assert "dit_attn3d_noalloc" in _err() and "NULL" in _err()
+    assert L.dit_attn3d_noalloc(o, q, k, v, 65, 2, 128, None, 2, 0, 1, None) == dit.DIT_E_INVAL
+    assert L.dit_attn3d_noalloc(o, q, k, v, 64, 2, 96, None, 1, 0, 1, None) == dit.DIT_E_UNSUPPORTED
+    assert L.dit_attn3d_noalloc(o, q, k, v, 64, 2, 128, FAKE * 32, 2, 0, 1, None) == dit.DIT_E_INVAL
+    assert L.dit_attn3d_noalloc(q, q, k, v, 64, 2, 128, None, 1, 0, 1, None) == dit.DIT_E_INVAL
+    assert "overlap" in _err()
+    assert L.dit_attn3d_noalloc(o, q, k, v, 64, 2, 128, None, 1, 0, 7, None) == dit.DIT_E_UNSUPPORTED
+
+
 def test_attn_lse_validation():
     L = ensure_built()
     o, lse, q, k, v = FAKE * 16, FAKE * 24, FAKE, FAKE * 4, FAKE * 8
