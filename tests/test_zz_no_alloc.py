@@ -81,3 +81,35 @@ def test_noalloc_float32():
     w = _workload("na_f32", "f32", (300, 77), 2, 64, seed=74)
     _, o_ref, o_na = _both(w)
     assert torch.equal(o_ref, o_na)
+
+
+def test_noalloc_graph_replays_bitwise():
+    """Captured into a graph (its clear kernel and its persistent launch, with the
+    scratch slot's address baked in) and replayed three times, with eager calls of
+    both entry points and synchronisations between the replays: every replay
+    equals the eager allocation-free result bit for bit, so the slot is cleared
+    for each replay and left clean for the eager calls."""
+    need_gpu()
+    w = _workload("na_graph", "bf16", (8192,), 40, 128, seed=75)
+    inp = synth.make(w, ["q", "k", "v"])
+    q, k, v = (dev(inp[n], w) for n in ("q", "k", "v"))
+    eager = torch.empty_like(q)
+    dit.dit_attn3d_noalloc(eager, q, k, v)
+    torch.cuda.synchronize()
+    cap = torch.empty_like(q)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dit.dit_attn3d_noalloc(cap, q, k, v)
+    ref = torch.empty_like(q)
+    for r in range(3):
+        cap.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cap, eager), r
+        again = torch.empty_like(q)
+        dit.dit_attn3d_noalloc(again, q, k, v)
+        dit.dit_attn3d(ref, q, k, v)
+        torch.cuda.synchronize()
+        assert torch.equal(again, eager), r
+    note(f"noalloc graph: 3 replays bitwise equal to the eager call ({w.tokens} tokens x {w.heads} heads)")
